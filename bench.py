@@ -1,0 +1,267 @@
+"""Benchmark of the mixed-precision KV transfer path on one MI355X.
+
+One step = the whole path over one request of the Mistral-7B-shaped workload
+(32 layers, 32 query / 8 KV heads, head dim 128, 8192 tokens, S = 4 sinks,
+3-tier, b = 0.5): per layer the two score passes (row log-sum-exp, then the
+MFMA column sums accumulated into the score), tier assignment, pack, dense
+unpack and paged unpack (16-token blocks, seeded permuted block table).
+Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is the fp16-equivalent KV throughput of
+pack + dense unpack, 2 * KV_fp16_bytes / (t_pack + t_unpack), from HIP events
+recorded on the launch stream inside the timed steps; the score's TFLOP/s and
+every stage's time are reported beside it.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="mistral7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="rough budget of the oracle's timed sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the transfer path is built and timed on a "
+              "single MI355X (multi-GPU sharding is a design note, not a measured path).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import serving_sk_score_amd as sk
+    from workloads import gen, get_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sk.lib()  # fails loudly if the HIP library is not built
+
+    cfg = get_config(args.workload)
+    L, Hq, Hkv, d, n = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.tokens
+    dev = torch.device("cuda", 0)
+    log(f"workload {cfg.name}: L={L} Hq={Hq} Hkv={Hkv} d={d} n={n}; generating inputs")
+    t0 = time.time()
+    from concurrent.futures import ThreadPoolExecutor
+
+    Q = torch.empty((L, n, Hq, d), dtype=torch.float16, device=dev)
+    K = torch.empty((L, n, Hkv, d), dtype=torch.float16, device=dev)
+    V = torch.empty((L, n, Hkv, d), dtype=torch.float16, device=dev)
+
+    def layer_inputs(layer):
+        k = gen.keys(cfg, layer)
+        return gen.queries(cfg, layer, k=k), k, gen.values(cfg, layer)
+
+    with ThreadPoolExecutor(16) as ex:
+        for layer, (q, k, v) in enumerate(ex.map(layer_inputs, range(L))):
+            Q[layer].copy_(torch.from_numpy(q))
+            K[layer].copy_(torch.from_numpy(k))
+            V[layer].copy_(torch.from_numpy(v))
+    torch.cuda.synchronize()
+    log(f"inputs resident in {time.time() - t0:.1f} s")
+
+    shape = sk.Shape(L, Hq, Hkv, d)
+    shape1 = sk.Shape(1, Hq, Hkv, d)
+    pol = sk.Policy(n, cfg.sinks, cfg.three_tier, cfg.budget)
+    plan = sk.plan_make(shape, pol)
+    lse = torch.empty((Hq, n), dtype=torch.float32, device=dev)
+    cws = torch.empty(max(1, sk.colsum_workspace_bytes(shape1, n)), dtype=torch.uint8, device=dev)
+    score = torch.empty(n, dtype=torch.float32, device=dev)
+    amap = torch.empty(n, dtype=torch.int32, device=dev)
+    order = torch.empty(n, dtype=torch.int32, device=dev)
+    payload = torch.empty(plan.payload_bytes, dtype=torch.uint8, device=dev)
+    Ko = torch.empty_like(K)
+    Vo = torch.empty_like(V)
+    bs = 16
+    nblk = (n + bs - 1) // bs
+    perm = np.random.default_rng(0).permutation(nblk).astype(np.int32)
+    block_table = torch.from_numpy(perm).to(dev)
+    Kc = torch.empty((L, nblk, bs, Hkv, d), dtype=torch.float16, device=dev)
+    Vc = torch.empty_like(Kc)
+
+    stages = ["rowlse", "colsum", "assign", "pack", "unpack", "unpack_paged"]
+    ev = None
+
+    def mark(name, i):
+        if ev is not None:
+            ev[name][i].record()
+
+    def step():
+        for layer in range(L):
+            mark("rowlse", 2 * layer)
+            sk.score_rowlse(shape1, Q[layer], K[layer], lse)
+            mark("rowlse", 2 * layer + 1)
+            mark("colsum", 2 * layer)
+            sk.score_colsum(shape1, Q[layer], K[layer], lse, score, layer > 0, cws)
+            mark("colsum", 2 * layer + 1)
+        mark("assign", 0)
+        sk.assign_tiers(pol, plan, score, amap, order)
+        mark("assign", 1)
+        mark("pack", 0)
+        sk.pack(shape, plan, K, V, amap, order, payload)
+        mark("pack", 1)
+        mark("unpack", 0)
+        sk.unpack(shape, plan, payload, amap, Ko, Vo)
+        mark("unpack", 1)
+        mark("unpack_paged", 0)
+        sk.unpack_paged(shape, plan, payload, amap, Kc, Vc, block_table, bs)
+        mark("unpack_paged", 1)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nev = {"rowlse": 2 * L, "colsum": 2 * L}
+    all_ev = [{s: [torch.cuda.Event(enable_timing=True) for _ in range(nev.get(s, 2))]
+               for s in stages} for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    wall0 = time.time()
+    start.record()
+    for i in range(args.steps):
+        ev = all_ev[i]
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # per stage: [steps][launches] durations in ms
+    t = {s: np.array([[e[s][2 * j].elapsed_time(e[s][2 * j + 1]) for j in range(len(e[s]) // 2)]
+                      for e in all_ev]) for s in stages}
+    mean_launch = {s: float(t[s].mean()) for s in stages}          # ms per launch
+    per_step_ms = {s: float(t[s].sum(axis=1).mean()) for s in stages}
+
+    kv_bytes = 2 * L * n * Hkv * d * 2
+    pack_bytes = kv_bytes + 4 * n + plan.payload_bytes                  # read K,V + map, write P
+    unpack_bytes = plan.payload_bytes + 4 * n + kv_bytes
+    t_pack = per_step_ms["pack"] * 1e-3
+    t_unpack = per_step_ms["unpack"] * 1e-3
+    t_paged = per_step_ms["unpack_paged"] * 1e-3
+    value = 2 * kv_bytes / (t_pack + t_unpack) / 1e9
+    pass_flops = Hq * d * n * (n + 1)                                   # one pass, one layer
+    score_s = (per_step_ms["rowlse"] + per_step_ms["colsum"]) * 1e-3
+    score_tflops = 2 * pass_flops * L / score_s / 1e12
+
+    dom = "colsum" if mean_launch["colsum"] >= mean_launch["rowlse"] else "rowlse"
+    ach = pass_flops / (mean_launch[dom] * 1e-3) / 1e12
+    kernel_name = {"colsum": "colsum_kernel<128,4>", "rowlse": "rowlse_kernel<128,4>"}[dom]
+
+    def rl(bytes_, sec):
+        gbs = bytes_ / sec / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    line = {
+        "metric": "KV pack+unpack GB/s (fp16-equiv, % HBM peak); importance-score TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: L={L} Hq={Hq} Hkv={Hkv} d={d} n={n} S={cfg.sinks} "
+                               f"b={cfg.budget} {'3' if cfg.three_tier else '2'}-tier",
+                   "tokens": n, "layers": L, "budget": cfg.budget, "paged_block": bs},
+        "pack_unpack_pct_hbm": round((pack_bytes + unpack_bytes) / (t_pack + t_unpack) / 1e9
+                                     / HBM_PEAK_GBS, 4),
+        "score_tflops": round(score_tflops, 1),
+        "score_pct_mfma": round(score_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "stage_ms_per_step": {s: round(v, 4) for s, v in per_step_ms.items()},
+        "payload_bytes": plan.payload_bytes,
+        "counts": {"fp16": plan.n16, "int8": plan.n8, "int4": plan.n4},
+        "roofline": {"bound": "mfma", "kernel": kernel_name, "achieved": round(ach, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": pass_flops,
+                     "avg_launch_ms": round(mean_launch[dom], 4)},
+        "roofline_stages": {"pack": rl(pack_bytes, t_pack), "unpack": rl(unpack_bytes, t_unpack),
+                            "unpack_paged": rl(unpack_bytes, t_paged)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle, as it stands, timed on the host cores on a bounded sample of
+    the same workload; reported in the metric's unit."""
+    from oracle import assign as OA, plan as OP, quant as OQ, score as OS
+    from workloads import gen
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas = None
+    cores = len(os.sched_getaffinity(0))
+    L, Hq, Hkv, d, n = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.tokens
+    opl = OP.make_plan(L, Hq, Hkv, d, n, cfg.sinks, cfg.budget, cfg.three_tier)
+    # pack + unpack of whole layers until about half the budget is spent
+    k = gen.keys(cfg, 0)
+    v = gen.values(cfg, 0)
+    s32 = np.random.default_rng(0).random(n).astype(np.float32)
+    t0 = time.time()
+    _, _, amap, _ = OA.assign(s32, opl.n16, opl.n8, opl.n4, opl.sinks)
+    t_assign = time.time() - t0
+    layers = 0
+    t_pu = 0.0
+    buf = np.zeros(opl.payload_bytes, dtype=np.uint8)
+    while t_pu < budget_s / 2 and layers < L:
+        t0 = time.time()
+        for off, data in OQ.pack_layer(k, v, layers, amap, opl):
+            buf[off:off + data.size] = data
+        OQ.unpack_layer(buf, layers, amap, opl, Hkv, d)
+        t_pu += time.time() - t0
+        layers += 1
+    kv_layer = 2 * n * Hkv * d * 2
+    gbs = 2 * kv_layer * layers / t_pu / 1e9
+    # score: whole (layer, head) pairs in fp64 until the other half is spent
+    q = gen.queries(cfg, 0, k=k)
+    heads = 0
+    t_sc = 0.0
+    while t_sc < budget_s / 2 and heads < Hq:
+        t0 = time.time()
+        OS.head_column_sums(q[:, heads, :], k[:, heads // (Hq // Hkv), :])
+        t_sc += time.time() - t0
+        heads += 1
+    tflops = heads * d * n * (n + 1) / t_sc / 1e12          # single-pass QK^T count
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "blas_threads": blas,
+            "kind": "oracle",
+            "sample": f"pack+unpack of {layers} of {L} layers (fp16-equiv GB/s, numpy, "
+                      f"1 thread); score of {heads} (layer, head) pairs of {L * Hq} in fp64",
+            "score_tflops": round(tflops, 6), "assign_s_full": round(t_assign, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * sk.h - C ABI of the per-token mixed-precision KV transfer path on MI355X.
+ *
+ * The operations follow the SpectrumKV paper (arXiv 2606.08635):
+ *   - importance score            : §4.3 (I_j = A_j with lambda = 0) and
+ *                                    Algorithm 1 "score tokens"
+ *   - tier assignment             : §4.4 budget-to-tier mapping, §7.4.1 sink
+ *                                    pinning, §2.3 Proposition 1 (sorted
+ *                                    assignment), Algorithm 1 "assign tiers"
+ *   - quantize + pack             : Algorithm 1 "transfer" (K and V quantized
+ *                                    independently, one mixed payload), §2.1
+ *                                    tier costs
+ *   - dequantize (dense or paged) : §4.2 (decode-side dequantization only)
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     never allocates, frees or synchronizes, and keeps no pointer after a
+ *     call returns.  It has no global mutable state except the per-thread
+ *     error message.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Device work is enqueued asynchronously on it.
+ *   - Validation: all arguments are checked on the host before anything is
+ *     enqueued.  On any error nothing is enqueued, no output is touched and a
+ *     non-zero status is returned; sk_last_error() then describes it.
+ *   - Device errors: a failed launch returns SK_E_DEVICE.  Faults inside a
+ *     kernel surface at the caller's next synchronization.
+ *   - Pointers to device memory must be 16-byte aligned; `payload` must be
+ *     256-byte aligned.  All tensors are dense and row-major as documented.
+ *   - Element types: fp16 = IEEE binary16, fp32 = IEEE binary32, little-endian.
+ *   - n_tokens = 0 is a valid, empty request: every call returns SK_OK and
+ *     enqueues nothing.
+ */
+#ifndef SK_H_
+#define SK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sk_status;
+#define SK_OK            0
+#define SK_E_ARG         1  /* NULL / misaligned pointer, bad size, bad value */
+#define SK_E_UNSUPPORTED 2  /* shape the kernels do not handle (head_dim, ...) */
+#define SK_E_BUDGET      3  /* budget cannot pay every token at the cheapest tier */
+#define SK_E_WORKSPACE   4  /* workspace smaller than the *_workspace_bytes query */
+#define SK_E_DEVICE      5  /* a HIP launch failed */
+
+#define SK_LAYOUT_V1 1
+#define SK_TIER_FP16 0u
+#define SK_TIER_INT8 1u
+#define SK_TIER_INT4 2u
+#define SK_MAP_TIER(m) ((uint32_t)(m) >> 30)
+#define SK_MAP_SLOT(m) ((uint32_t)(m) & 0x3FFFFFFFu)
+
+/* Model KV shape (§2.1: L layers, H_kv KV heads of dimension d_h; GQA query
+ * head h reads KV head h / (n_q_heads / n_kv_heads)).
+ * Supported: n_layers >= 1, n_kv_heads >= 1, n_q_heads a multiple of
+ * n_kv_heads with n_q_heads / n_kv_heads <= 16, head_dim in {64, 128, 256}. */
+typedef struct {
+    int32_t n_layers;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+} sk_shape;
+
+/* Transfer policy of one request.
+ *   n_tokens   : n, 0 <= n < 2^30
+ *   n_sink     : S >= 0, leading tokens pinned to fp16 (§7.4.1)
+ *   three_tier : 1 = fp16/int8/int4 (int4 probe passed, §4.5), 0 = fp16/int8
+ *   budget     : b in [0, 1], fraction of the fp16 bytes (§2.1, §4.4) */
+typedef struct {
+    int64_t n_tokens;
+    int32_t n_sink;
+    int32_t three_tier;
+    double  budget;
+} sk_policy;
+
+/* Tier counts and payload layout, a pure function of (shape, policy).
+ *
+ * Counts (§4.4 and §7.4.1; quarter-token units fp16 = 4, int8 = 2, int4 = 1):
+ *   B  = floor(4 b n + 1e-7) evaluated in double,  S' = min(S, n),
+ *   R  = n - S',  Br = B - 4 S'   (sinks are paid from the budget first)
+ *   3-tier: Br < R -> SK_E_BUDGET;  Br <= 2R -> n16 = 0, n8 = Br - R,
+ *           n4 = 2R - Br (the printed f8 = 4b-1, f4 = 2-4b); otherwise
+ *           n16 = min(R, floor((Br - 2R)/2)), n8 = R - n16, n4 = 0.
+ *   2-tier: Br < 2R -> SK_E_BUDGET; otherwise as the upper 3-tier branch.
+ *   N16 = S' + n16, N8 = n8, N4 = n4.
+ *
+ * Payload layout v1 (no padding): segments c16 | c8 | c4 | s8 | s4.
+ *   A "row" is (layer l, slot, kv in {0 = K, 1 = V}, KV head g) of head_dim
+ *   elements; within tier t its index is r = ((l * N_t + slot) * 2 + kv) * H + g.
+ *   c16 : fp16 rows, 2d bytes each            (raw copy of the input)
+ *   c8  : int8 two's complement codes, d bytes each
+ *   c4  : int4 two's complement codes, d/2 bytes each, element 2m in bits
+ *         0-3 and element 2m+1 in bits 4-7 of byte m
+ *   s8, s4 : one fp16 scale per int8 / int4 row, same row order
+ *   payload_bytes = L * 2H * (N16 * 2d + N8 * (d + 2) + N4 * (d/2 + 2)). */
+typedef struct {
+    int64_t n16, n8, n4;        /* n16 includes the sinks */
+    int64_t n_sink;             /* S' */
+    int64_t budget_units;       /* B */
+    int64_t used_units;         /* 4 N16 + 2 N8 + N4 <= B */
+    int64_t payload_bytes;
+    int64_t off_c16, off_c8, off_c4, off_s8, off_s4;
+    int64_t n_tokens;
+    int32_t n_layers, n_kv_heads, head_dim, layout_version;
+    uint64_t check;             /* hash of every field above; sk_pack and
+                                   sk_unpack reject a plan whose hash or
+                                   shape does not match */
+} sk_plan;
+
+/* Host only, pure, touches no device.  Returns SK_E_ARG / SK_E_UNSUPPORTED
+ * for a bad shape or policy and SK_E_BUDGET when the budget cannot pay every
+ * token (out is then left untouched). */
+sk_status sk_plan_make(const sk_shape* shape, const sk_policy* policy, sk_plan* out);
+
+/* ---------------------------------------------------------------- score --
+ * Importance score of one layer (§4.3 with lambda = 0, Algorithm 1):
+ *   A_j = sum_h sum_{i >= j} softmax_i(q_i . k_j / sqrt(d))_j,
+ * the causal attention column sums of layer l over its H_q query heads.
+ * Calling it once per layer with accumulate = (l > 0) yields
+ * score_j = sum_l A_j (the attention received over all heads and layers).
+ *
+ *   q     : fp16 [n][n_q_heads][head_dim]  (this layer's post-RoPE queries)
+ *   k     : fp16 [n][n_kv_heads][head_dim] (this layer's post-RoPE keys)
+ *   score : fp32 [n]; overwritten (accumulate = 0) or added to (1)
+ *   ws    : device workspace of at least sk_score_workspace_bytes(shape, n)
+ *           bytes; its contents are scratch between calls.
+ * Two passes run back to back on `stream`: a row log-sum-exp pass and a
+ * column-sum pass that recomputes q.k with MFMA and sums exp(s - lse); the
+ * per-KV-head partial sums are then added in a fixed order, so the result
+ * is deterministic. */
+size_t    sk_score_workspace_bytes(const sk_shape* shape, int64_t n_tokens);
+sk_status sk_score(const sk_shape* shape, int64_t n_tokens,
+                   const void* q, const void* k, float* score, int32_t accumulate,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* The two passes of sk_score as separate calls (same results when chained).
+ *   sk_score_rowlse : lse fp32 [n_q_heads][n], lse[h][i] =
+ *                     ln sum_{j <= i} exp(q_i . k_j / sqrt(d))  (natural log)
+ *   sk_score_colsum : uses lse from sk_score_rowlse on the same q, k and
+ *                     writes / accumulates score as sk_score does; ws must
+ *                     hold sk_score_colsum_workspace_bytes(shape, n) bytes. */
+sk_status sk_score_rowlse(const sk_shape* shape, int64_t n_tokens,
+                          const void* q, const void* k, float* lse, void* stream);
+size_t    sk_score_colsum_workspace_bytes(const sk_shape* shape, int64_t n_tokens);
+sk_status sk_score_colsum(const sk_shape* shape, int64_t n_tokens,
+                          const void* q, const void* k, const float* lse,
+                          float* score, int32_t accumulate,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------- assign --
+ * Tier assignment (§7.4.1 sinks, §2.3 sorted assignment, §4.4 counts):
+ * tokens j < S' get fp16; the others are ranked by (score descending, token
+ * index ascending) - ties go to the lower index - and the first n16 - S'
+ * take fp16, the next n8 int8 and the rest int4.
+ *   score : fp32 [n], finite and >= 0 (-0.0 counts as +0.0; NaN/Inf: the
+ *           output is unspecified but every write stays in bounds)
+ *   map   : u32 [n], map[j] = tier << 30 | slot, slot = number of tokens
+ *           j' < j with the same tier
+ *   order : u32 [n], the tokens sorted by (tier, index): fp16 slots first,
+ *           then int8, then int4; order[off_t + slot] = j
+ *   ws    : at least sk_assign_workspace_bytes(n) bytes. */
+size_t    sk_assign_workspace_bytes(int64_t n_tokens);
+sk_status sk_assign_tiers(const sk_policy* policy, const sk_plan* plan,
+                          const float* score, uint32_t* map, uint32_t* order,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------- pack --
+ * Quantize + compact (Algorithm 1 "transfer").  Per row of d elements:
+ * fp16 rows are copied; int8 / int4 rows use a symmetric absmax scale
+ *   s = fp16_rne(fl32(max|x| / qmax)),  qmax = 127 / 7,
+ *   q = clamp(rint_even(fl32(x / s)), -qmax, qmax)   (q = 0 when s == 0),
+ * written at the row's slot in the layout described at sk_plan.
+ *   k, v    : fp16 [n_layers][n][n_kv_heads][head_dim]
+ *   map     : from sk_assign_tiers (entries whose slot is out of range for
+ *             their tier are skipped)
+ *   order   : from sk_assign_tiers (may be NULL; reserved for layouts that
+ *             need it)
+ *   payload : plan->payload_bytes bytes, 256-byte aligned; every byte is
+ *             written when map is a valid assignment. */
+sk_status sk_pack(const sk_shape* shape, const sk_plan* plan,
+                  const void* k, const void* v,
+                  const uint32_t* map, const uint32_t* order,
+                  void* payload, void* stream);
+
+/* --------------------------------------------------------------- unpack --
+ * Decode side (§4.2): x_hat = fp16_rne(float(q) * float(s)) for int rows,
+ * the raw fp16 row otherwise.
+ * Dense:  paged == NULL, k_out / v_out fp16 [n_layers][n][n_kv_heads][head_dim]
+ *         (every element written).
+ * Paged:  k_out = v_out = NULL; token j of layer l is written to
+ *         cache[l][block_table[j / block_size]][j % block_size][g][:] of
+ *         k_cache and v_cache, both fp16
+ *         [n_layers][num_blocks][block_size][n_kv_heads][head_dim].  Rows of
+ *         blocks that hold no token of this request are untouched; a token
+ *         whose block id lies outside [0, num_blocks) is skipped. */
+typedef struct {
+    void* k_cache;
+    void* v_cache;
+    const int32_t* block_table;   /* device, [ceil(n / block_size)] */
+    int32_t block_size;           /* >= 1 */
+    int64_t num_blocks;           /* >= ceil(n / block_size) */
+} sk_paged;
+
+sk_status sk_unpack(const sk_shape* shape, const sk_plan* plan,
+                    const void* payload, const uint32_t* map,
+                    void* k_out, void* v_out, const sk_paged* paged, void* stream);
+
+/* ------------------------------------------------------------ messages -- */
+const char* sk_status_string(sk_status status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* sk_last_error(void);
+/* Layout version implemented (SK_LAYOUT_V1). */
+int32_t sk_layout_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SK_H_ */

@@ -58,7 +58,8 @@ def quantize_rows(x, qmax):
 def dequantize_rows(codes, s16):
     """codes int [..., d], s16 fp16 [...] -> fp16 [..., d] (one rounding)."""
     prod = np.asarray(codes).astype(np.float32) * np.asarray(s16, dtype=np.float16).astype(np.float32)[..., None]
-    return prod.astype(np.float16)
+    with np.errstate(over="ignore"):     # |q s| above 65504 rounds to +-inf, as IEEE fp16 does
+        return prod.astype(np.float16)
 
 
 def encode_int4(codes):

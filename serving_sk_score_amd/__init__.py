@@ -1,0 +1,13 @@
+"""MI355X-native per-token mixed-precision KV transfer path (SpectrumKV).
+
+The path - importance score, tier assignment, quantize + pack, dense or paged
+unpack - runs in hand-written HIP kernels for gfx950 behind the C ABI in
+``include/sk.h`` (``libsk.so``).  :mod:`serving_sk_score_amd.sk` is the thin
+Python binding; PyTorch only provides device memory and streams.
+"""
+
+from .sk import (  # noqa: F401
+    Plan, Policy, Shape, SkError, assign_tiers, colsum_workspace_bytes, lib, pack,
+    plan_make, score, score_colsum, score_rowlse, score_workspace_bytes, unpack,
+    unpack_paged,
+)

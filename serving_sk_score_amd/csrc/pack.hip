@@ -1,0 +1,278 @@
+// Quantize + compaction pack and dequantizing unpack (dense and paged).
+//
+// SpectrumKV paper, Algorithm 1 "transfer": K and V of every token are
+// quantized independently per its precision tier and sent as one payload;
+// §4.2: the decode worker only dequantizes.  Quantizer: symmetric absmax with
+// one fp16 scale per (layer, token, K|V, KV head) row of d elements.
+//
+// Mapping to CDNA4: one wavefront owns one (layer, token) and walks its 2*H
+// rows (K heads then V heads).  A row of d fp16 values is spread over d/8
+// lanes, each holding 8 consecutive elements (one 16-byte load), so a wave
+// covers 64/(d/8) rows per step and every global access is a contiguous
+// 16/8/4-byte vector per lane.  The absmax is a butterfly max over the lanes
+// of a row.  The tier is uniform across the wave, so there is no divergence
+// between the fp16 copy and the int8/int4 paths.
+//
+// Exact arithmetic: the scale needs one correctly rounded fp32 division per
+// row (a / qmax) and one for r = 1/s.  Each element then uses
+//   q0 = x*r,  e = fma(-q0, s, x),  q1 = fma(e, r, q0)
+// which equals the correctly rounded quotient fl32(x/s) for every pair of
+// fp16 x and fp16 s with |x/s| <= 300 (Markstein's correction step; checked
+// exhaustively over all such pairs), so rint(q1) is bit-identical to
+// rint(fl32(x/s)) without a per-element division.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "sk_kernels.h"
+
+namespace sk {
+namespace {
+
+constexpr int kWaves = 4;  // wavefronts (tokens) per workgroup
+
+struct Segs {
+    int64_t cnt[3];
+    int64_t oc[3];
+    int64_t os[3];
+};
+
+Segs make_segs(const TierSeg seg[3]) {
+    Segs s;
+    for (int t = 0; t < 3; ++t) {
+        s.cnt[t] = seg[t].count;
+        s.oc[t] = seg[t].off_code;
+        s.os[t] = seg[t].off_scale;
+    }
+    return s;
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xFFFFu)));
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// Quantize 8 elements of one row whose absmax over the whole row is `a`.
+template <int QMAX>
+__device__ __forceinline__ void quant8(const float (&x)[8], float a, int (&q)[8],
+                                       uint32_t& sbits) {
+    const float s32 = a / (float)QMAX;  // IEEE division
+    const __half s16 = __float2half_rn(s32);
+    sbits = __half_as_ushort(s16);
+    const float s = __half2float(s16);
+    if (s == 0.0f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = 0;
+        return;
+    }
+    const float r = 1.0f / s;  // IEEE division
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float q0 = x[e] * r;
+        const float err = fmaf(-q0, s, x[e]);
+        const float q1 = fmaf(err, r, q0);
+        float t = rintf(q1);
+        t = fminf(fmaxf(t, -(float)QMAX), (float)QMAX);
+        q[e] = (int)t;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void pack_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint32_t* __restrict__ map, uint8_t* __restrict__ out, Segs sg, int64_t n,
+    int H) {
+    constexpr int LPR = D / 8;    // lanes per row
+    constexpr int RPP = 64 / LPR; // rows per step
+    const int lane = threadIdx.x & 63;
+    const int64_t j = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t layer = blockIdx.y;
+    if (j >= n) return;
+    const uint32_t m = map[j];
+    const uint32_t t = m >> 30;
+    const int64_t slot = m & 0x3FFFFFFFu;
+    if (t > 2u || slot >= sg.cnt[t]) return;
+    const int part = lane % LPR;
+    const int rows = 2 * H;
+    const int64_t rowbase = (layer * sg.cnt[t] + slot) * rows;
+    const int64_t tokrow = (layer * n + j) * H;
+
+    for (int r0 = 0; r0 < rows; r0 += RPP) {
+        const int r = r0 + lane / LPR;
+        if (r >= rows) break;  // whole row-groups leave together
+        const uint16_t* src = (r < H ? K : V) + (tokrow + (r < H ? r : r - H)) * D + part * 8;
+        const uint4 raw = *reinterpret_cast<const uint4*>(src);
+        const int64_t row = rowbase + r;
+        if (t == 0u) {
+            *reinterpret_cast<uint4*>(out + sg.oc[0] + row * (2 * D) + part * 16) = raw;
+            continue;
+        }
+        float x[8];
+        x[0] = h2f(raw.x);
+        x[1] = h2f(raw.x >> 16);
+        x[2] = h2f(raw.y);
+        x[3] = h2f(raw.y >> 16);
+        x[4] = h2f(raw.z);
+        x[5] = h2f(raw.z >> 16);
+        x[6] = h2f(raw.w);
+        x[7] = h2f(raw.w >> 16);
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
+        a = group_max<LPR>(a);
+        int q[8];
+        uint32_t sbits;
+        if (t == 1u) {
+            quant8<127>(x, a, q, sbits);
+            uint2 w;
+            w.x = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) |
+                  ((uint32_t)(q[3] & 0xFF) << 24);
+            w.y = (q[4] & 0xFF) | ((q[5] & 0xFF) << 8) | ((q[6] & 0xFF) << 16) |
+                  ((uint32_t)(q[7] & 0xFF) << 24);
+            *reinterpret_cast<uint2*>(out + sg.oc[1] + row * D + part * 8) = w;
+        } else {
+            quant8<7>(x, a, q, sbits);
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w |= (uint32_t)(q[e] & 0xF) << (4 * e);
+            *reinterpret_cast<uint32_t*>(out + sg.oc[2] + row * (D / 2) + part * 4) = w;
+        }
+        if (part == 0)
+            *reinterpret_cast<uint16_t*>(out + sg.os[t] + row * 2) = (uint16_t)sbits;
+    }
+}
+
+__device__ __forceinline__ uint32_t deq_pair(int q0, int q1, float s) {
+    const __half a = __float2half_rn((float)q0 * s);  // exact product, one rounding
+    const __half b = __float2half_rn((float)q1 * s);
+    return (uint32_t)__half_as_ushort(a) | ((uint32_t)__half_as_ushort(b) << 16);
+}
+
+__device__ __forceinline__ int sext8(uint32_t w, int byte) {
+    return (int)(int8_t)((w >> (8 * byte)) & 0xFFu);
+}
+
+__device__ __forceinline__ int sext4(uint32_t w, int nib) {
+    return ((int)(w << (28 - 4 * nib))) >> 28;
+}
+
+// Dequantize the row part of lane `part` for tier t into 8 fp16 values.
+template <int D>
+__device__ __forceinline__ uint4 load_row_part(const uint8_t* __restrict__ in,
+                                               const Segs& sg, uint32_t t, int64_t row,
+                                               int part) {
+    if (t == 0u)
+        return *reinterpret_cast<const uint4*>(in + sg.oc[0] + row * (2 * D) + part * 16);
+    const float s = h2f(*reinterpret_cast<const uint16_t*>(in + sg.os[t] + row * 2));
+    uint4 o;
+    if (t == 1u) {
+        const uint2 w = *reinterpret_cast<const uint2*>(in + sg.oc[1] + row * D + part * 8);
+        o.x = deq_pair(sext8(w.x, 0), sext8(w.x, 1), s);
+        o.y = deq_pair(sext8(w.x, 2), sext8(w.x, 3), s);
+        o.z = deq_pair(sext8(w.y, 0), sext8(w.y, 1), s);
+        o.w = deq_pair(sext8(w.y, 2), sext8(w.y, 3), s);
+    } else {
+        const uint32_t w =
+            *reinterpret_cast<const uint32_t*>(in + sg.oc[2] + row * (D / 2) + part * 4);
+        o.x = deq_pair(sext4(w, 0), sext4(w, 1), s);
+        o.y = deq_pair(sext4(w, 2), sext4(w, 3), s);
+        o.z = deq_pair(sext4(w, 4), sext4(w, 5), s);
+        o.w = deq_pair(sext4(w, 6), sext4(w, 7), s);
+    }
+    return o;
+}
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kWaves * 64) void unpack_kernel(
+    const uint8_t* __restrict__ in, const uint32_t* __restrict__ map, Segs sg, int64_t n,
+    int H, uint16_t* __restrict__ Ko, uint16_t* __restrict__ Vo,
+    const int32_t* __restrict__ block_table, int32_t block_size, int64_t num_blocks) {
+    constexpr int LPR = D / 8;
+    constexpr int RPP = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int64_t j = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t layer = blockIdx.y;
+    if (j >= n) return;
+    const uint32_t m = map[j];
+    const uint32_t t = m >> 30;
+    const int64_t slot = m & 0x3FFFFFFFu;
+    if (t > 2u || slot >= sg.cnt[t]) return;
+    int64_t dstrow;  // row index of head 0 of this token in the output
+    if (PAGED) {
+        const int64_t blk = block_table[j / block_size];
+        if (blk < 0 || blk >= num_blocks) return;
+        dstrow = ((layer * num_blocks + blk) * block_size + (j % block_size)) * H;
+    } else {
+        dstrow = (layer * n + j) * H;
+    }
+    const int part = lane % LPR;
+    const int rows = 2 * H;
+    const int64_t rowbase = (layer * sg.cnt[t] + slot) * rows;
+    for (int r0 = 0; r0 < rows; r0 += RPP) {
+        const int r = r0 + lane / LPR;
+        if (r >= rows) break;
+        const uint4 o = load_row_part<D>(in, sg, t, rowbase + r, part);
+        uint16_t* dst = (r < H ? Ko : Vo) + (dstrow + (r < H ? r : r - H)) * D + part * 8;
+        *reinterpret_cast<uint4*>(dst) = o;
+    }
+}
+
+template <typename F>
+hipError_t dispatch_d(int d, F&& f) {
+    switch (d) {
+        case 64: return f(std::integral_constant<int, 64>{});
+        case 128: return f(std::integral_constant<int, 128>{});
+        case 256: return f(std::integral_constant<int, 256>{});
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const Dims& s, const TierSeg seg[3], const void* k, const void* v,
+                       const uint32_t* map, void* payload, hipStream_t st) {
+    const Segs sg = make_segs(seg);
+    const dim3 grid((unsigned)((s.n + kWaves - 1) / kWaves), (unsigned)s.L);
+    return dispatch_d(s.d, [&](auto D) {
+        hipLaunchKernelGGL((pack_kernel<decltype(D)::value>), grid, dim3(kWaves * 64), 0, st,
+                           (const uint16_t*)k, (const uint16_t*)v, map, (uint8_t*)payload, sg,
+                           s.n, s.Hkv);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_unpack_dense(const Dims& s, const TierSeg seg[3], const void* payload,
+                               const uint32_t* map, void* k_out, void* v_out,
+                               hipStream_t st) {
+    const Segs sg = make_segs(seg);
+    const dim3 grid((unsigned)((s.n + kWaves - 1) / kWaves), (unsigned)s.L);
+    return dispatch_d(s.d, [&](auto D) {
+        hipLaunchKernelGGL((unpack_kernel<decltype(D)::value, false>), grid, dim3(kWaves * 64),
+                           0, st, (const uint8_t*)payload, map, sg, s.n, s.Hkv,
+                           (uint16_t*)k_out, (uint16_t*)v_out, (const int32_t*)nullptr, 1,
+                           (int64_t)0);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_unpack_paged(const Dims& s, const TierSeg seg[3], const void* payload,
+                               const uint32_t* map, void* k_cache, void* v_cache,
+                               const int32_t* block_table, int32_t block_size,
+                               int64_t num_blocks, hipStream_t st) {
+    const Segs sg = make_segs(seg);
+    const dim3 grid((unsigned)((s.n + kWaves - 1) / kWaves), (unsigned)s.L);
+    return dispatch_d(s.d, [&](auto D) {
+        hipLaunchKernelGGL((unpack_kernel<decltype(D)::value, true>), grid, dim3(kWaves * 64),
+                           0, st, (const uint8_t*)payload, map, sg, s.n, s.Hkv,
+                           (uint16_t*)k_cache, (uint16_t*)v_cache, block_table, block_size,
+                           num_blocks);
+        return hipGetLastError();
+    });
+}
+
+}  // namespace sk

@@ -1,0 +1,219 @@
+// Tier assignment: sink pinning + importance-sorted fp16/int8/int4 split.
+//
+// SpectrumKV paper, §7.4.1 and Algorithm 1: the first S tokens are pinned to
+// fp16 before ranking; the others are sorted by importance and filled into
+// fp16, int8 and (optionally) int4 with the counts of the §4.4 budget mapping.
+// §2.3 Proposition 1: any such sorted assignment minimises the
+// importance-weighted error for fixed counts.  Ties go to the lower token
+// index.
+//
+// Method.  A token's rank only matters through two thresholds: the k1-th and
+// the k2-th largest key among the non-sink tokens, k1 = n16 - S', k2 = k1 + n8.
+// Keys are unique integers key = (score bits << b) | (2^b - 1 - j), where
+// b = bits needed to hold n, so a larger key means a higher score or, on a
+// tie, a lower index; for non-negative floats the IEEE bit pattern is
+// monotone.  Both thresholds are found with one MSB-first radix select
+// (8-bit digits, LDS histograms, one workgroup) - each pass narrows the
+// prefix of both thresholds at once.  A token is fp16 iff key >= K_k1, int8
+// iff not fp16 and key >= K_k2, int4 otherwise.  Slots (positions among the
+// same tier in token order) come from wavefront ballots and a workgroup
+// prefix over 1024-token tiles; order[] is the inverse permutation.
+//
+// Histogram contention: the top digits of nearby scores coincide, so every
+// thread first merges runs of equal digits in registers and issues one LDS
+// atomic per run.
+#include <hip/hip_runtime.h>
+
+#include "sk_kernels.h"
+
+namespace sk {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ uint64_t make_key(float s, int64_t j, int bits) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;  // -0.0 ranks as +0.0
+    return ((uint64_t)u << bits) | (uint64_t)(((int64_t)1 << bits) - 1 - j);
+}
+
+// Within one wavefront: given 256 bins, find the digit D (scanning from the
+// top) where the cumulative count first reaches k.  Returns D and the count
+// of keys strictly above D.
+__device__ void find_digit(const uint32_t* hist, uint64_t k, int lane, int* out_digit,
+                           uint64_t* out_above) {
+    // lane holds digits 255-4*lane .. 252-4*lane (descending)
+    uint32_t c[4];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        c[e] = hist[255 - 4 * lane - e];
+        tot += c[e];
+    }
+    // inclusive prefix over lanes (lane 0 = highest digits)
+    uint32_t incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    const uint32_t excl = incl - tot;
+    const bool here = (excl < k) && (incl >= k);
+    const unsigned long long who = __ballot(here);
+    const int src = __ffsll((long long)who) - 1;
+    if (lane == src) {
+        uint32_t run = excl;
+        int digit = 0;
+        uint32_t above = excl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (run + c[e] >= k) {
+                digit = 255 - 4 * lane - e;
+                above = run;
+                break;
+            }
+            run += c[e];
+        }
+        *out_digit = digit;
+        *out_above = above;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void select_kernel(
+    const float* __restrict__ score, int64_t n, int64_t sinks, int64_t k1, int64_t k2,
+    int64_t n16, int64_t n8, uint32_t* __restrict__ map, uint32_t* __restrict__ order) {
+    __shared__ uint32_t hist[2][256];
+    __shared__ uint64_t prefix[2];
+    __shared__ uint64_t krem[2];
+    __shared__ int sel_digit[2];
+    __shared__ uint64_t sel_above[2];
+    __shared__ uint32_t wcnt[kWaves][3];
+    __shared__ uint32_t running[3];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t R = n - sinks;
+
+    int bits = 1;
+    while (((int64_t)1 << bits) < n) ++bits;
+    const int total_bits = 32 + bits;
+    const int passes = (total_bits + 7) / 8;
+
+    // selection s in {0, 1} is active when 1 <= k_s <= R
+    const int64_t ks[2] = {k1, k2};
+    bool active[2];
+    for (int s = 0; s < 2; ++s) active[s] = ks[s] >= 1 && ks[s] <= R;
+    if (tid == 0) {
+        for (int s = 0; s < 2; ++s) {
+            prefix[s] = 0;
+            krem[s] = (uint64_t)(active[s] ? ks[s] : 1);
+        }
+    }
+    uint64_t pmask = 0;  // bits of the key fixed so far (uniform)
+
+    for (int p = 0; p < passes && (active[0] || active[1]); ++p) {
+        const int shift = 8 * (passes - 1 - p);
+        for (int i = tid; i < 512; i += kThreads) (&hist[0][0])[i] = 0;
+        __syncthreads();
+        const uint64_t pre0 = prefix[0], pre1 = prefix[1];
+        int run_d0 = -1, run_d1 = -1;
+        uint32_t run_c0 = 0, run_c1 = 0;
+        for (int64_t j = sinks + tid; j < n; j += kThreads) {
+            const uint64_t key = make_key(score[j], j, bits);
+            const int dg = (int)((key >> shift) & 0xFFu);
+            if (active[0] && (key & pmask) == pre0) {
+                if (dg != run_d0) {
+                    if (run_c0) atomicAdd(&hist[0][run_d0], run_c0);
+                    run_d0 = dg;
+                    run_c0 = 0;
+                }
+                ++run_c0;
+            }
+            if (active[1] && (key & pmask) == pre1) {
+                if (dg != run_d1) {
+                    if (run_c1) atomicAdd(&hist[1][run_d1], run_c1);
+                    run_d1 = dg;
+                    run_c1 = 0;
+                }
+                ++run_c1;
+            }
+        }
+        if (run_c0) atomicAdd(&hist[0][run_d0], run_c0);
+        if (run_c1) atomicAdd(&hist[1][run_d1], run_c1);
+        __syncthreads();
+        if (wave < 2 && active[wave]) {
+            find_digit(hist[wave], krem[wave], lane, &sel_digit[wave], &sel_above[wave]);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int s = 0; s < 2; ++s) {
+                if (!active[s]) continue;
+                prefix[s] |= (uint64_t)sel_digit[s] << shift;
+                krem[s] -= sel_above[s];
+            }
+        }
+        pmask |= (uint64_t)0xFFu << shift;
+        __syncthreads();
+    }
+
+    const uint64_t K1 = prefix[0], K2 = prefix[1];
+    // cond_s(key): rank < k_s  (k_s = 0 -> false, k_s > R -> true)
+    const bool all1 = k1 > R, none1 = k1 <= 0;
+    const bool all2 = k2 > R, none2 = k2 <= 0;
+    const uint32_t base[3] = {0u, (uint32_t)n16, (uint32_t)(n16 + n8)};
+    if (tid < 3) running[tid] = 0;
+    __syncthreads();
+    for (int64_t t0 = 0; t0 < n; t0 += kThreads) {
+        const int64_t j = t0 + tid;
+        int tier = -1;
+        if (j < n) {
+            if (j < sinks) {
+                tier = 0;
+            } else {
+                const uint64_t key = make_key(score[j], j, bits);
+                const bool c1 = !none1 && (all1 || key >= K1);
+                const bool c2 = !none2 && (all2 || key >= K2);
+                tier = c1 ? 0 : (c2 ? 1 : 2);
+            }
+        }
+        uint32_t mypre = 0;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const unsigned long long b = __ballot(tier == t);
+            if (lane == 0) wcnt[wave][t] = (uint32_t)__popcll(b);
+            if (tier == t) mypre = (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
+        }
+        __syncthreads();
+        if (tier >= 0) {
+            uint32_t off = running[tier];
+            for (int w = 0; w < wave; ++w) off += wcnt[w][tier];
+            const uint32_t slot = off + mypre;
+            map[j] = ((uint32_t)tier << 30) | slot;
+            order[base[tier] + slot] = (uint32_t)j;
+        }
+        __syncthreads();
+        if (tid < 3) {
+            uint32_t s = 0;
+            for (int w = 0; w < kWaves; ++w) s += wcnt[w][tid];
+            running[tid] += s;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_select(int64_t n, int64_t sinks, int64_t n16, int64_t n8, int64_t n4,
+                         const float* score, uint32_t* map, uint32_t* order,
+                         hipStream_t st) {
+    (void)n4;
+    const int64_t k1 = n16 - sinks;
+    const int64_t k2 = k1 + n8;
+    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kThreads), 0, st, score, n, sinks, k1, k2,
+                       n16, n8, map, order);
+    return hipGetLastError();
+}
+
+}  // namespace sk

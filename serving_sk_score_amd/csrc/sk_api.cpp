@@ -1,0 +1,345 @@
+// C-ABI layer: argument validation, the tier-count / layout closed form and
+// dispatch to the HIP kernels.  Nothing is enqueued unless every check passes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/sk.h"
+#include "sk_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sk_status fail(sk_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+sk_status ok() {
+    g_err.clear();
+    return SK_OK;
+}
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+sk_status check_shape(const sk_shape* s) {
+    if (!s) return fail(SK_E_ARG, "shape is NULL");
+    if (s->n_layers < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1)
+        return fail(SK_E_ARG, "shape: n_layers, n_q_heads and n_kv_heads must be >= 1");
+    if (s->n_q_heads % s->n_kv_heads)
+        return fail(SK_E_ARG, "shape: n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                    s->n_q_heads, s->n_kv_heads);
+    if (s->n_q_heads / s->n_kv_heads > 16)
+        return fail(SK_E_UNSUPPORTED, "shape: more than 16 query heads per KV head");
+    if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256)
+        return fail(SK_E_UNSUPPORTED, "shape: head_dim %d not in {64, 128, 256}", s->head_dim);
+    if (s->n_layers > 65535) return fail(SK_E_UNSUPPORTED, "shape: more than 65535 layers");
+    return SK_OK;
+}
+
+sk_status check_tokens(int64_t n) {
+    if (n < 0 || n >= kMaxTokens) return fail(SK_E_ARG, "n_tokens %lld outside [0, 2^30)", (long long)n);
+    return SK_OK;
+}
+
+uint64_t plan_hash(const sk_plan& p) {
+    const int64_t f[] = {p.n16, p.n8, p.n4, p.n_sink, p.budget_units, p.used_units,
+                         p.payload_bytes, p.off_c16, p.off_c8, p.off_c4, p.off_s8, p.off_s4,
+                         p.n_tokens, p.n_layers, p.n_kv_heads, p.head_dim, p.layout_version};
+    uint64_t h = 1469598103934665603ull;  // FNV-1a
+    for (int64_t v : f) {
+        for (int b = 0; b < 8; ++b) {
+            h ^= (uint64_t)((v >> (8 * b)) & 0xFF);
+            h *= 1099511628211ull;
+        }
+    }
+    return h;
+}
+
+sk_status check_plan(const sk_plan* p, const sk_shape* s) {
+    if (!p) return fail(SK_E_ARG, "plan is NULL");
+    if (p->layout_version != SK_LAYOUT_V1) return fail(SK_E_ARG, "plan: unknown layout version");
+    if (p->check != plan_hash(*p)) return fail(SK_E_ARG, "plan: checksum mismatch (corrupted plan)");
+    if (s && (p->n_layers != s->n_layers || p->n_kv_heads != s->n_kv_heads ||
+              p->head_dim != s->head_dim))
+        return fail(SK_E_ARG, "plan was made for a different shape");
+    return SK_OK;
+}
+
+sk::Dims dims(const sk_shape* s, int64_t n) {
+    return sk::Dims{s->n_layers, s->n_q_heads, s->n_kv_heads, s->head_dim, n};
+}
+
+void segs(const sk_plan* p, sk::TierSeg seg[3]) {
+    seg[0] = {p->n16, p->off_c16, 0};
+    seg[1] = {p->n8, p->off_c8, p->off_s8};
+    seg[2] = {p->n4, p->off_c4, p->off_s4};
+}
+
+sk_status device(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SK_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t lse_bytes(const sk_shape* s, int64_t n) {
+    return align256((size_t)s->n_q_heads * (size_t)n * sizeof(float));
+}
+
+size_t partial_bytes(const sk_shape* s, int64_t n) {
+    const sk::Dims d = dims(s, n);
+    return align256((size_t)sk::colsum_partial_rows(d) * (size_t)sk::padded_tokens(n) *
+                    sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sk_layout_version(void) { return SK_LAYOUT_V1; }
+
+const char* sk_status_string(sk_status st) {
+    switch (st) {
+        case SK_OK: return "SK_OK";
+        case SK_E_ARG: return "SK_E_ARG: invalid argument";
+        case SK_E_UNSUPPORTED: return "SK_E_UNSUPPORTED: unsupported shape";
+        case SK_E_BUDGET: return "SK_E_BUDGET: budget cannot pay every token";
+        case SK_E_WORKSPACE: return "SK_E_WORKSPACE: workspace too small";
+        case SK_E_DEVICE: return "SK_E_DEVICE: HIP launch failed";
+        default: return "unknown sk_status";
+    }
+}
+
+const char* sk_last_error(void) { return g_err.c_str(); }
+
+sk_status sk_plan_make(const sk_shape* shape, const sk_policy* pol, sk_plan* out) {
+    if (sk_status st = check_shape(shape)) return st;
+    if (!pol || !out) return fail(SK_E_ARG, "policy and out must be non-NULL");
+    if (sk_status st = check_tokens(pol->n_tokens)) return st;
+    if (pol->n_sink < 0) return fail(SK_E_ARG, "n_sink must be >= 0");
+    if (pol->three_tier != 0 && pol->three_tier != 1)
+        return fail(SK_E_ARG, "three_tier must be 0 or 1");
+    if (!std::isfinite(pol->budget) || pol->budget < 0.0 || pol->budget > 1.0)
+        return fail(SK_E_ARG, "budget must be a finite fraction in [0, 1]");
+
+    const int64_t n = pol->n_tokens;
+    const int64_t S = pol->n_sink < n ? pol->n_sink : n;
+    const int64_t R = n - S;
+    // quarter-token units: fp16 = 4, int8 = 2, int4 = 1
+    const int64_t B = (int64_t)std::floor(4.0 * pol->budget * (double)n + 1e-7);
+    const int64_t Br = B - 4 * S;
+    int64_t n16 = 0, n8 = 0, n4 = 0;
+    if (pol->three_tier) {
+        if (Br < R)
+            return fail(SK_E_BUDGET, "budget %.6g pays %lld quarter units for %lld tokens",
+                        pol->budget, (long long)Br, (long long)R);
+        if (Br <= 2 * R) {
+            n8 = Br - R;
+            n4 = 2 * R - Br;
+        } else {
+            n16 = (Br - 2 * R) / 2;
+            if (n16 > R) n16 = R;
+            n8 = R - n16;
+        }
+    } else {
+        if (Br < 2 * R)
+            return fail(SK_E_BUDGET, "2-tier budget %.6g pays %lld quarter units for %lld tokens",
+                        pol->budget, (long long)Br, (long long)R);
+        n16 = (Br - 2 * R) / 2;
+        if (n16 > R) n16 = R;
+        n8 = R - n16;
+    }
+    sk_plan p;
+    std::memset(&p, 0, sizeof(p));
+    p.n16 = S + n16;
+    p.n8 = n8;
+    p.n4 = n4;
+    p.n_sink = S;
+    p.budget_units = B;
+    p.used_units = 4 * p.n16 + 2 * p.n8 + p.n4;
+    const int64_t L = shape->n_layers, H = shape->n_kv_heads, d = shape->head_dim;
+    const int64_t rows16 = L * p.n16 * 2 * H, rows8 = L * p.n8 * 2 * H, rows4 = L * p.n4 * 2 * H;
+    p.off_c16 = 0;
+    p.off_c8 = p.off_c16 + rows16 * 2 * d;
+    p.off_c4 = p.off_c8 + rows8 * d;
+    p.off_s8 = p.off_c4 + rows4 * (d / 2);
+    p.off_s4 = p.off_s8 + rows8 * 2;
+    p.payload_bytes = p.off_s4 + rows4 * 2;
+    p.n_tokens = n;
+    p.n_layers = shape->n_layers;
+    p.n_kv_heads = shape->n_kv_heads;
+    p.head_dim = shape->head_dim;
+    p.layout_version = SK_LAYOUT_V1;
+    p.check = plan_hash(p);
+    *out = p;
+    return ok();
+}
+
+size_t sk_score_colsum_workspace_bytes(const sk_shape* shape, int64_t n) {
+    if (check_shape(shape) || check_tokens(n)) return 0;
+    return partial_bytes(shape, n);
+}
+
+size_t sk_score_workspace_bytes(const sk_shape* shape, int64_t n) {
+    if (check_shape(shape) || check_tokens(n)) return 0;
+    return lse_bytes(shape, n) + partial_bytes(shape, n);
+}
+
+static sk_status check_score_io(const sk_shape* shape, int64_t n, const void* q, const void* k) {
+    if (sk_status st = check_shape(shape)) return st;
+    if (sk_status st = check_tokens(n)) return st;
+    if (n > 0 && (!q || !k)) return fail(SK_E_ARG, "q and k must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16)) return fail(SK_E_ARG, "q and k must be 16-byte aligned");
+    return SK_OK;
+}
+
+sk_status sk_score_rowlse(const sk_shape* shape, int64_t n, const void* q, const void* k,
+                          float* lse, void* stream) {
+    if (sk_status st = check_score_io(shape, n, q, k)) return st;
+    if (n > 0 && !lse) return fail(SK_E_ARG, "lse must be non-NULL");
+    if (!aligned(lse, 4)) return fail(SK_E_ARG, "lse must be 4-byte aligned");
+    if (n == 0) return ok();
+    (void)hipGetLastError();
+    return device(sk::launch_rowlse(dims(shape, n), q, k, lse, (hipStream_t)stream), "rowlse");
+}
+
+sk_status sk_score_colsum(const sk_shape* shape, int64_t n, const void* q, const void* k,
+                          const float* lse, float* score, int32_t accumulate, void* ws,
+                          size_t ws_bytes, void* stream) {
+    if (sk_status st = check_score_io(shape, n, q, k)) return st;
+    if (n > 0 && (!lse || !score)) return fail(SK_E_ARG, "lse and score must be non-NULL");
+    if (!aligned(lse, 4) || !aligned(score, 4)) return fail(SK_E_ARG, "lse and score must be 4-byte aligned");
+    if (accumulate != 0 && accumulate != 1) return fail(SK_E_ARG, "accumulate must be 0 or 1");
+    if (n == 0) return ok();
+    const size_t need = partial_bytes(shape, n);
+    if (!ws || ws_bytes < need)
+        return fail(SK_E_WORKSPACE, "colsum workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");
+    const sk::Dims d = dims(shape, n);
+    (void)hipGetLastError();
+    hipError_t e = sk::launch_colsum(d, q, k, lse, (float*)ws, (hipStream_t)stream);
+    if (e != hipSuccess) return device(e, "colsum");
+    return device(sk::launch_reduce(d, (const float*)ws, score, accumulate, (hipStream_t)stream),
+                  "reduce");
+}
+
+sk_status sk_score(const sk_shape* shape, int64_t n, const void* q, const void* k, float* score,
+                   int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+    if (sk_status st = check_score_io(shape, n, q, k)) return st;
+    if (n > 0 && !score) return fail(SK_E_ARG, "score must be non-NULL");
+    if (!aligned(score, 4)) return fail(SK_E_ARG, "score must be 4-byte aligned");
+    if (accumulate != 0 && accumulate != 1) return fail(SK_E_ARG, "accumulate must be 0 or 1");
+    if (n == 0) return ok();
+    const size_t need = lse_bytes(shape, n) + partial_bytes(shape, n);
+    if (!ws || ws_bytes < need)
+        return fail(SK_E_WORKSPACE, "score workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");
+    const sk::Dims d = dims(shape, n);
+    float* lse = (float*)ws;
+    float* partial = (float*)((char*)ws + lse_bytes(shape, n));
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipError_t e = sk::launch_rowlse(d, q, k, lse, st);
+    if (e != hipSuccess) return device(e, "rowlse");
+    e = sk::launch_colsum(d, q, k, lse, partial, st);
+    if (e != hipSuccess) return device(e, "colsum");
+    return device(sk::launch_reduce(d, partial, score, accumulate, st), "reduce");
+}
+
+size_t sk_assign_workspace_bytes(int64_t n) {
+    (void)n;
+    return 0;
+}
+
+sk_status sk_assign_tiers(const sk_policy* pol, const sk_plan* plan, const float* score,
+                          uint32_t* map, uint32_t* order, void* ws, size_t ws_bytes,
+                          void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!pol) return fail(SK_E_ARG, "policy is NULL");
+    if (sk_status st = check_plan(plan, nullptr)) return st;
+    if (plan->n_tokens != pol->n_tokens) return fail(SK_E_ARG, "plan and policy disagree on n_tokens");
+    if (plan->n_sink != (pol->n_sink < pol->n_tokens ? pol->n_sink : pol->n_tokens))
+        return fail(SK_E_ARG, "plan and policy disagree on n_sink");
+    const int64_t n = plan->n_tokens;
+    if (n == 0) return ok();
+    if (!score || !map || !order) return fail(SK_E_ARG, "score, map and order must be non-NULL");
+    if (!aligned(score, 4) || !aligned(map, 4) || !aligned(order, 4))
+        return fail(SK_E_ARG, "score, map and order must be 4-byte aligned");
+    (void)hipGetLastError();
+    return device(sk::launch_select(n, plan->n_sink, plan->n16, plan->n8, plan->n4, score, map,
+                                    order, (hipStream_t)stream),
+                  "select");
+}
+
+sk_status sk_pack(const sk_shape* shape, const sk_plan* plan, const void* k, const void* v,
+                  const uint32_t* map, const uint32_t* order, void* payload, void* stream) {
+    (void)order;
+    if (sk_status st = check_shape(shape)) return st;
+    if (sk_status st = check_plan(plan, shape)) return st;
+    const int64_t n = plan->n_tokens;
+    if (n == 0) return ok();
+    if (!k || !v || !map || !payload) return fail(SK_E_ARG, "k, v, map and payload must be non-NULL");
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(SK_E_ARG, "k and v must be 16-byte aligned");
+    if (!aligned(map, 4)) return fail(SK_E_ARG, "map must be 4-byte aligned");
+    if (!aligned(payload, 256)) return fail(SK_E_ARG, "payload must be 256-byte aligned");
+    sk::TierSeg seg[3];
+    segs(plan, seg);
+    (void)hipGetLastError();
+    return device(sk::launch_pack(dims(shape, n), seg, k, v, map, payload, (hipStream_t)stream),
+                  "pack");
+}
+
+sk_status sk_unpack(const sk_shape* shape, const sk_plan* plan, const void* payload,
+                    const uint32_t* map, void* k_out, void* v_out, const sk_paged* paged,
+                    void* stream) {
+    if (sk_status st = check_shape(shape)) return st;
+    if (sk_status st = check_plan(plan, shape)) return st;
+    const int64_t n = plan->n_tokens;
+    if (paged) {
+        if (k_out || v_out) return fail(SK_E_ARG, "paged unpack takes k_out = v_out = NULL");
+        if (paged->block_size < 1) return fail(SK_E_ARG, "block_size must be >= 1");
+        if (paged->num_blocks < (n + paged->block_size - 1) / paged->block_size)
+            return fail(SK_E_ARG, "num_blocks smaller than ceil(n / block_size)");
+    }
+    if (n == 0) return ok();
+    if (!payload || !map) return fail(SK_E_ARG, "payload and map must be non-NULL");
+    if (!aligned(payload, 256)) return fail(SK_E_ARG, "payload must be 256-byte aligned");
+    if (!aligned(map, 4)) return fail(SK_E_ARG, "map must be 4-byte aligned");
+    sk::TierSeg seg[3];
+    segs(plan, seg);
+    const sk::Dims d = dims(shape, n);
+    (void)hipGetLastError();
+    if (!paged) {
+        if (!k_out || !v_out) return fail(SK_E_ARG, "dense unpack needs k_out and v_out");
+        if (!aligned(k_out, 16) || !aligned(v_out, 16))
+            return fail(SK_E_ARG, "k_out and v_out must be 16-byte aligned");
+        return device(sk::launch_unpack_dense(d, seg, payload, map, k_out, v_out,
+                                              (hipStream_t)stream),
+                      "unpack");
+    }
+    if (!paged->k_cache || !paged->v_cache || !paged->block_table)
+        return fail(SK_E_ARG, "paged unpack needs k_cache, v_cache and block_table");
+    if (!aligned(paged->k_cache, 16) || !aligned(paged->v_cache, 16) ||
+        !aligned(paged->block_table, 4))
+        return fail(SK_E_ARG, "paged caches must be 16-byte aligned, block_table 4-byte aligned");
+    return device(sk::launch_unpack_paged(d, seg, payload, map, paged->k_cache, paged->v_cache,
+                                          paged->block_table, paged->block_size,
+                                          paged->num_blocks, (hipStream_t)stream),
+                  "unpack");
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launchers of the HIP kernels behind include/sk.h.  Every launcher
+// assumes its arguments were validated by the C-ABI layer (sk_api.cpp) and
+// only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sk {
+
+struct Dims {
+    int32_t L, Hq, Hkv, d;
+    int64_t n;
+};
+
+// Layout of one tier's rows inside the payload.
+struct TierSeg {
+    int64_t count;     // N_t
+    int64_t off_code;  // byte offset of the code segment
+    int64_t off_scale; // byte offset of the scale segment (int tiers)
+};
+
+// score pass 1: lse fp32 [Hq][n] (natural log)
+hipError_t launch_rowlse(const Dims& s, const void* q, const void* k, float* lse,
+                         hipStream_t st);
+// score pass 2: partial fp32 [Hkv][n_pad], n_pad = padded_tokens(n)
+hipError_t launch_colsum(const Dims& s, const void* q, const void* k, const float* lse,
+                         float* partial, hipStream_t st);
+// score[j] = (acc ? score[j] : 0) + sum_g partial[g][j], g in order
+hipError_t launch_reduce(const Dims& s, const float* partial, float* score, int acc,
+                         hipStream_t st);
+int64_t padded_tokens(int64_t n);
+// number of rows of the pass-2 partial buffer
+int colsum_partial_rows(const Dims& s);
+
+// tier selection
+hipError_t launch_select(int64_t n, int64_t sinks, int64_t n16, int64_t n8, int64_t n4,
+                         const float* score, uint32_t* map, uint32_t* order,
+                         hipStream_t st);
+
+// pack / unpack
+hipError_t launch_pack(const Dims& s, const TierSeg seg[3], const void* k, const void* v,
+                       const uint32_t* map, void* payload, hipStream_t st);
+hipError_t launch_unpack_dense(const Dims& s, const TierSeg seg[3], const void* payload,
+                               const uint32_t* map, void* k_out, void* v_out,
+                               hipStream_t st);
+hipError_t launch_unpack_paged(const Dims& s, const TierSeg seg[3], const void* payload,
+                               const uint32_t* map, void* k_cache, void* v_cache,
+                               const int32_t* block_table, int32_t block_size,
+                               int64_t num_blocks, hipStream_t st);
+
+}  // namespace sk
