@@ -100,6 +100,21 @@ def main():
     Kc = torch.empty((L, nblk, bs, Hkv, d), dtype=torch.float16, device=dev)
     Vc = torch.empty_like(Kc)
 
+    # practical bandwidth ceiling (and the counter calibration kernel of the
+    # traffic measurement): a device-to-device copy of the K+V bytes
+    src = K.view(-1).view(torch.uint8)
+    dst = torch.empty_like(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    c0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 3 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del dst
+
     stages = ["rowlse", "colsum", "assign", "pack", "unpack", "unpack_paged"]
     ev = None
 
@@ -169,12 +184,14 @@ def main():
 
     dom = "colsum" if mean_launch["colsum"] >= mean_launch["rowlse"] else "rowlse"
     ach = pass_flops / (mean_launch[dom] * 1e-3) / 1e12
-    kernel_name = {"colsum": "colsum_kernel<128,4>", "rowlse": "rowlse_kernel<128,4>"}[dom]
+    W = 4 if Hq // Hkv == 4 else Hq // Hkv   # heads per workgroup of the launch timed
+    kernel_name = f"{dom}_kernel<{d},{W}>"
 
-    def rl(bytes_, sec):
+    def rl(bytes_, sec, kernel):
         gbs = bytes_ / sec / 1e9
-        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": bytes_,
+                "traffic": counted_traffic(kernel)}
 
     line = {
         "metric": "KV pack+unpack GB/s (fp16-equiv, % HBM peak); importance-score TFLOP/s",
@@ -201,16 +218,42 @@ def main():
         "counts": {"fp16": plan.n16, "int8": plan.n8, "int4": plan.n4},
         "roofline": {"bound": "mfma", "kernel": kernel_name, "achieved": round(ach, 1),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": counted_traffic(kernel_name),
                      "flops_per_launch": pass_flops,
                      "avg_launch_ms": round(mean_launch[dom], 4)},
-        "roofline_stages": {"pack": rl(pack_bytes, t_pack), "unpack": rl(unpack_bytes, t_unpack),
-                            "unpack_paged": rl(unpack_bytes, t_paged)},
+        "roofline_stages": {"pack": rl(pack_bytes, t_pack, f"pack_kernel<{d}>"),
+                            "unpack": rl(unpack_bytes, t_unpack, f"unpack_kernel<{d},dense>"),
+                            "unpack_paged": rl(unpack_bytes, t_paged, f"unpack_kernel<{d},paged>")},
+        "copy_ceiling_gbs": round(copy_gbs, 1),
+        "copy_bytes": int(src.numel()),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def counted_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summaries (FETCH_SIZE + WRITE_SIZE, calibrated against a device copy), or
+    None when no summary covers it or its source file changed since."""
+    import glob
+    import hashlib
+    import re
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    pat = re.compile(r"<!-- traffic kernel=(\S+) bytes_per_launch=(\d+) source=(\S+) sha256=([0-9a-f]+) -->")
+    for path in sorted(glob.glob(os.path.join(root, "profiles", "*.md"))):
+        for m in pat.finditer(open(path).read()):
+            if m.group(1) != kernel:
+                continue
+            src = os.path.join(root, m.group(3))
+            if not os.path.exists(src):
+                continue
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() == m.group(4):
+                return int(m.group(2))
+    return None
 
 
 def cpu_baseline(cfg, budget_s):
