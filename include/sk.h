@@ -131,16 +131,19 @@ sk_status sk_plan_make(const sk_shape* shape, const sk_policy* policy, sk_plan* 
  *           bytes; its contents are scratch between calls.
  * Two passes run back to back on `stream`: a row log-sum-exp pass and a
  * column-sum pass that recomputes q.k with MFMA and sums exp(s - lse); the
- * per-KV-head partial sums are then added in a fixed order, so the result
- * is deterministic. */
+ * per-query-head partial sums are then added in a fixed order, so the
+ * result is deterministic. */
 size_t    sk_score_workspace_bytes(const sk_shape* shape, int64_t n_tokens);
 sk_status sk_score(const sk_shape* shape, int64_t n_tokens,
                    const void* q, const void* k, float* score, int32_t accumulate,
                    void* ws, size_t ws_bytes, void* stream);
 
 /* The two passes of sk_score as separate calls (same results when chained).
- *   sk_score_rowlse : lse fp32 [n_q_heads][n], lse[h][i] =
- *                     ln sum_{j <= i} exp(q_i . k_j / sqrt(d))  (natural log)
+ *   sk_score_rowlse : lse fp32 [n_q_heads][n], the base-2 logarithm of the
+ *                     causal softmax denominator of row i of head h:
+ *                     lse[h][i] = log2 sum_{j <= i} exp(q_i . k_j / sqrt(d))
+ *                     (= the natural log-sum-exp times log2(e)); base 2 lets
+ *                     the column pass weight each element with one exp2.
  *   sk_score_colsum : uses lse from sk_score_rowlse on the same q, k and
  *                     writes / accumulates score as sk_score does; ws must
  *                     hold sk_score_colsum_workspace_bytes(shape, n) bytes. */

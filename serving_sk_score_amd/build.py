@@ -32,6 +32,9 @@ FLAGS = [
     # rounded fp32 division
     "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # MFMA results in architectural VGPRs: the softmax reads them directly
+    # instead of copying each element out of an AGPR first
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
     "-Wno-unused-function",
     f"-I{INCLUDE}",

@@ -7,38 +7,53 @@
 //
 // The softmax of row i needs the whole row before any column can be summed,
 // and storing P is O(n^2), so the path is two passes over Q K^T:
-//   pass 1 (rowlse): lse[h][i] = ln sum_{j<=i} exp(s_ij), online max/sum;
-//   pass 2 (colsum): recompute s_ij and sum exp(s_ij - lse_i) down each
-//                    column j, per KV head group; a fixed-order reduction over
-//                    groups then yields the layer's A_j.
+//   pass 1 (rowlse): lse2[h][i] = log2 sum_{j<=i} exp(q_i . k_j / sqrt(d)),
+//                    the base-2 logarithm of the causal softmax denominator;
+//   pass 2 (colsum): recompute s_ij and sum 2^(c2 s_ij - lse2_i) down each
+//                    column j (c2 = log2(e)/sqrt(d)), per query head; a
+//                    fixed-order reduction over heads yields the layer's A_j.
 // Both passes are dense fp16 contractions on v_mfma_f32_32x32x16_f16 with
-// fp32 accumulation; the softmax arithmetic is fp32 in base 2
-// (exp2(s * log2(e)/sqrt(d) - m)).
+// fp32 accumulation; the softmax arithmetic is fp32 in base 2.
 //
 // MFMA 32x32x16 operand layout (per 64-lane wavefront):
 //   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
 //   B (16 x 32): lane l holds column l%32, k = 8*(l/32) .. +7
 //   C (32 x 32): lane l holds column l%32, rows 8*(e/4) + 4*(l/32) + e%4, e = 0..15
 // A and B are both "k-contiguous", which is exactly the row-major [token][d]
-// layout of Q and K, so fragments are single 16-byte reads.
+// layout of Q and K, so every fragment is one 16-byte read.
+//
+// Cost model on gfx950 (per 32x32 tile and wavefront, measured): the d/16
+// MFMAs take 2d cycles of the matrix pipe; the softmax work is 16 elements
+// per lane at one fma + one exp2 + one add each (~12 cycles per element
+// row).  At d >= 128 the VALU work fits under the MFMA work when the two
+// overlap, so both passes keep two wavefronts per SIMD, prefetch the next
+// LDS stage while computing on the current one (double buffering, one
+// barrier per stage) and keep per-element work to those three operations.
 //
 // pass 1 computes S^T = K Q^T (rows = keys, columns = queries): each lane owns
-// one query and 16 of the 32 keys of a tile, so the row max / row sum are
-// in-lane plus one exchange with lane l^32.  A workgroup is the W query heads
-// of one GQA group (one wavefront each) over the same 64 queries, so each K
-// tile is staged once in LDS and read by all W heads.
+// one query and 16 of the 32 keys of a tile, so the row sums are in-lane; the
+// two half-waves' partial sums are combined once at the end.  A workgroup is
+// W query heads of one GQA group times QW blocks of 64 queries (one wavefront
+// each), so each staged K tile is read by every wavefront.  The key stages on
+// the causal diagonal are processed first with the exact online max; they fix
+// a per-row reference m, and the remaining (unmasked) stages then only add
+// 2^(c2 s - m): no per-element max.  A tile whose sum exceeds 2^64 (a logit
+// far above the reference) is redone with the exact update, so the result
+// never overflows whatever the inputs.
 //
 // pass 2 computes S = Q K^T (rows = queries, columns = keys): each lane owns
 // one key column of each 32-key sub-tile, so the column sum is an in-lane
-// accumulation across all query tiles.  A workgroup keeps 64 keys of its
-// group stationary in registers (one wavefront per query head) and streams
-// the W heads' query tiles through LDS.
+// accumulation across all query tiles.  A workgroup is one query head and
+// KW wavefronts of 64 stationary keys each; the head's query tiles and their
+// lse2 values stream through LDS and are read by every wavefront.
 //
-// Work is causal (tile pairs above the diagonal are skipped) and workgroups
-// are launched longest-first; the KV group index runs fastest across the
-// grid so that consecutive workgroups (round-robin over the 8 XCDs) of one
-// group land on the same XCD and share its L2.
+// Work is causal (tiles above the diagonal are skipped) and workgroups are
+// launched longest-first.  In pass 1 the GQA group index runs fastest across
+// the grid, so with 8 groups each of the 8 XCDs serves one group's keys from
+// its own L2.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "sk_kernels.h"
 
@@ -48,17 +63,18 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMaxWaves = 8;
-constexpr int kQB = 64;   // queries per pass-1 workgroup (2 sub-tiles)
-constexpr int kKB = 64;   // keys per pass-2 workgroup (2 sub-tiles)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+// A pass-1 tile whose partial sum exceeds this goes through the exact update.
+constexpr float kTileLimit = 18446744073709551616.0f;  // 2^64
+constexpr int kStageKeys = 64;   // keys per pass-1 workgroup stage (32 for d = 256)
+constexpr int kColKeys = 64;     // stationary keys per pass-2 wavefront
+constexpr int kColWaves = 4;     // pass-2 wavefronts per workgroup
 
 __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ half8 zero8() {
     half8 z;
@@ -67,253 +83,401 @@ __device__ __forceinline__ half8 zero8() {
     return z;
 }
 
+__device__ __forceinline__ floatx16 zero16() {
+    floatx16 z;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+    return z;
+}
+
 // Row within a 32x32 C tile held by element e of lane l.
 __device__ __forceinline__ int crow(int e, int lane) {
     return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
 }
 
-// Cooperative staging of 32 tokens x NSEG*D halfs (contiguous per token in
+// Cooperative staging of ROWS tokens x D halfs (contiguous per token in
 // global memory, token stride `gstride` halfs) into LDS rows of D + 8 halfs
-// by NT threads.  LDS row index = seg * 32 + token (seg-major), so that the
-// MFMA fragment reads of 32 consecutive LDS rows at a fixed column are
-// bank-conflict free (row pitch = 4 banks mod 64).
-template <int D, int NSEG, int NT>
+// by NT threads, through registers so that the global loads of the next
+// stage are in flight while the current one is computed on.  The row pitch
+// of D + 8 halfs puts the 32 rows of an MFMA fragment read at distinct
+// bank groups.  Tokens at or beyond n are stored as zeros.
+template <int D, int ROWS, int NT>
 struct Stager {
-    static constexpr int kPieces = D / 8;                 // 16-byte pieces per segment
-    static constexpr int kTotal = 32 * NSEG * kPieces;
+    static constexpr int kPieces = D / 8;  // 16-byte pieces per row
+    static constexpr int kTotal = ROWS * kPieces;
     static constexpr int kRegs = (kTotal + NT - 1) / NT;
     uint4 regs[kRegs];
-    __device__ void load(int tid, const _Float16* __restrict__ g, int64_t t0, int64_t n,
-                         int64_t gstride) {
+    __device__ __forceinline__ void load(int tid, const _Float16* __restrict__ g, int64_t t0,
+                                         int64_t n, int64_t gstride) {
 #pragma unroll
         for (int r = 0; r < kRegs; ++r) {
             const int idx = tid + r * NT;
             uint4 v = make_uint4(0, 0, 0, 0);
             if (kTotal % NT == 0 || idx < kTotal) {
-                const int tok = idx / (NSEG * kPieces);
-                const int rem = idx % (NSEG * kPieces);
+                const int tok = idx / kPieces;
+                const int piece = idx % kPieces;
                 if (t0 + tok < n)
-                    v = *reinterpret_cast<const uint4*>(g + (t0 + tok) * gstride + rem * 8);
+                    v = *reinterpret_cast<const uint4*>(g + (t0 + tok) * gstride + piece * 8);
             }
             regs[r] = v;
         }
     }
-    __device__ void store(int tid, _Float16* lds) const {
+    __device__ __forceinline__ void store(int tid, _Float16* lds) const {
 #pragma unroll
         for (int r = 0; r < kRegs; ++r) {
             const int idx = tid + r * NT;
             if (kTotal % NT == 0 || idx < kTotal) {
-                const int tok = idx / (NSEG * kPieces);
-                const int rem = idx % (NSEG * kPieces);
-                const int seg = rem / kPieces, piece = rem % kPieces;
-                *reinterpret_cast<uint4*>(lds + (seg * 32 + tok) * (D + 8) + piece * 8) =
-                    regs[r];
+                const int tok = idx / kPieces;
+                const int piece = idx % kPieces;
+                *reinterpret_cast<uint4*>(lds + tok * (D + 8) + piece * 8) = regs[r];
             }
         }
     }
 };
 
+// Sum over the 16 elements of a C tile of 2^(c2 x - m), in four chains.
+__device__ __forceinline__ float tile_expsum(const floatx16& a, float c2, float m) {
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+        s0 += ex2(fmaf(a[e + 0], c2, -m));
+        s1 += ex2(fmaf(a[e + 1], c2, -m));
+        s2 += ex2(fmaf(a[e + 2], c2, -m));
+        s3 += ex2(fmaf(a[e + 3], c2, -m));
+    }
+    return (s0 + s1) + (s2 + s3);
+}
+
+// Exact online-softmax update of one lane's (m, s) with the 16 elements of a
+// pass-1 C tile (rows = keys kt0 + crow, column = query qi).  With `masked`,
+// keys above the query are excluded.
+__device__ __forceinline__ void exact_update(const floatx16& a, float c2, bool masked,
+                                             int64_t kt0, int64_t qi, int lane, float& m,
+                                             float& s) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const bool keep = !masked || kt0 + crow(e, lane) <= qi;
+        mx = fmaxf(mx, keep ? a[e] * c2 : -INFINITY);
+    }
+    const float mn = fmaxf(m, mx);
+    if (mn == -INFINITY) return;
+    float acc = (m == -INFINITY) ? 0.0f : s * ex2(m - mn);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const bool keep = !masked || kt0 + crow(e, lane) <= qi;
+        acc += keep ? ex2(fmaf(a[e], c2, -mn)) : 0.0f;
+    }
+    s = acc;
+    m = mn;
+}
+
 // ---------------------------------------------------------------- pass 1 --
-template <int D, int W>
-__global__ __launch_bounds__(W * 64) void rowlse_kernel(
-    const _Float16* __restrict__ Q, const _Float16* __restrict__ K, float* __restrict__ lse,
+template <int D, int W, int QW, int KS>
+__global__ __launch_bounds__(W * QW * 64) void rowlse_kernel(
+    const _Float16* __restrict__ Q, const _Float16* __restrict__ K, float* __restrict__ lse2,
     int64_t n, int Hq, int Hkv, float c2) {
-    extern __shared__ _Float16 smem[];  // [32][D + 8]
+    constexpr int NT = W * QW * 64;
     constexpr int C = D / 16;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    constexpr int PITCH = D + 8;
+    constexpr int U = KS / 32;  // 32-key units per stage
+    extern __shared__ _Float16 smem[];  // [2][KS][PITCH]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int khalf = 8 * (lane >> 5);
     const int R = Hq / Hkv;
     const int chunks = R / W;
     const int g = blockIdx.x / chunks;
-    const int h = g * R + (blockIdx.x % chunks) * W + wave;
-    const int64_t nqb = gridDim.y;
-    const int64_t qb = nqb - 1 - blockIdx.y;  // longest rows first
-    const int64_t q0 = qb * kQB;
+    const int h = g * R + (blockIdx.x % chunks) * W + wave % W;
+    const int64_t QB = 64 * QW;
+    const int64_t Q0 = (int64_t)(gridDim.y - 1 - blockIdx.y) * QB;  // longest rows first
+    const int64_t q0 = Q0 + 64 * (wave / W);
 
     // stationary query fragments (B operand of S^T = K Q^T)
     half8 qf[2][C];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int64_t i = q0 + 32 * t + (lane & 31);
+        const int64_t i = q0 + 32 * t + col;
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            qf[t][c] = (i < n) ? *reinterpret_cast<const half8*>(
-                                     Q + (i * Hq + h) * D + c * 16 + 8 * (lane >> 5))
+        for (int c = 0; c < C; ++c)
+            qf[t][c] = (i < n) ? *reinterpret_cast<const half8*>(Q + (i * Hq + h) * D + c * 16 +
+                                                                 khalf)
                                : zero8();
-        }
     }
 
-    Stager<D, 1, W * 64> st;
-    const int tid = threadIdx.x;
+    // stages: first the ones on the diagonal ([Q0, qend)), then keys [0, Q0)
+    const int64_t qend = (Q0 + QB < n) ? Q0 + QB : n;
+    const int nd = (int)((qend - Q0 + KS - 1) / KS);
+    const int ns = nd + (int)(Q0 / KS);
+    auto key0 = [&](int s) -> int64_t {
+        return s < nd ? Q0 + (int64_t)KS * s : (int64_t)KS * (s - nd);
+    };
+
+    Stager<D, KS, NT> st;
     const _Float16* Kg = K + (int64_t)g * D;
     const int64_t kstride = (int64_t)Hkv * D;
-
-    const int64_t last_q = (q0 + kQB < n ? q0 + kQB : n) - 1;
-    const int64_t nkt = last_q / 32 + 1;  // key tiles 0 .. nkt-1
+    st.load(tid, Kg, key0(0), n, kstride);
+    st.store(tid, smem);
+    if (ns > 1) st.load(tid, Kg, key0(1), n, kstride);
+    __syncthreads();
 
     float m[2] = {-INFINITY, -INFINITY};
-    float sum[2] = {0.0f, 0.0f};
-
-    st.load(tid, Kg, 0, n, kstride);
-    for (int64_t kt = 0; kt < nkt; ++kt) {
-        __syncthreads();
-        st.store(tid, smem);
-        __syncthreads();
-        if (kt + 1 < nkt) st.load(tid, Kg, (kt + 1) * 32, n, kstride);
-
-        floatx16 acc[2];
-        const bool need[2] = {kt <= 2 * qb, kt <= 2 * qb + 1};
+    float s[2] = {0.0f, 0.0f};
+    for (int si = 0; si < ns; ++si) {
+        const _Float16* buf = smem + (si & 1) * (KS * PITCH);
+        const int64_t k0 = key0(si);
+        if (si < nd) {
+            // diagonal stages: masked, exact online max
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int u = 0; u < U; ++u) {
+                const int64_t kt0 = k0 + 32 * u;
+                const bool need0 = kt0 <= q0 + 31;
+                const bool need1 = kt0 <= q0 + 63;
+                if (!need1) continue;
+                floatx16 acc0 = zero16(), acc1 = zero16();
+                const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-        const _Float16* arow = smem + (lane & 31) * (D + 8) + 8 * (lane >> 5);
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
-            if (need[0]) acc[0] = mfma32(a, qf[0][c], acc[0]);
-            if (need[1]) acc[1] = mfma32(a, qf[1][c], acc[1]);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if (!need[t]) continue;
-            const bool diag = (kt == 2 * qb + t);
-            const int qcol = lane & 31;  // query offset within the tile
-            float x[16];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                x[e] = acc[t][e];
-                if (diag && crow(e, lane) > qcol) x[e] = -INFINITY;
-                mx = fmaxf(mx, x[e]);
+                for (int c = 0; c < C; ++c) {
+                    const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
+                    if (need0) acc0 = mfma32(a, qf[0][c], acc0);
+                    acc1 = mfma32(a, qf[1][c], acc1);
+                }
+                if (need0)
+                    exact_update(acc0, c2, kt0 + 31 > q0, kt0, q0 + col, lane, m[0], s[0]);
+                exact_update(acc1, c2, kt0 + 31 > q0 + 32, kt0, q0 + 32 + col, lane, m[1], s[1]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mnew = fmaxf(m[t], mx * c2);
-            float s = sum[t] * fast_exp2(m[t] - mnew);
+            if (si == nd - 1) {
+                // one reference per query row for the fast stages
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(x[e], c2, -mnew));
-            sum[t] = s;
-            m[t] = mnew;
+                for (int t = 0; t < 2; ++t) {
+                    float mn = fmaxf(m[t], __shfl_xor(m[t], 32, 64));
+                    if (mn == -INFINITY) mn = 0.0f;
+                    s[t] = (m[t] == -INFINITY) ? 0.0f : s[t] * ex2(m[t] - mn);
+                    m[t] = mn;
+                }
+            }
+        } else {
+            // stages strictly below the diagonal: no mask, fixed reference
+            floatx16 acc[U][2];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                acc[u][0] = zero16();
+                acc[u][1] = zero16();
+                const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
+                    acc[u][0] = mfma32(a, qf[0][c], acc[u][0]);
+                    acc[u][1] = mfma32(a, qf[1][c], acc[u][1]);
+                }
+            }
+            float ts[U][2];
+            bool ok = true;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    ts[u][t] = tile_expsum(acc[u][t], c2, m[t]);
+                    ok = ok && (ts[u][t] <= kTileLimit);
+                }
+            if (__builtin_expect(__all(ok), 1)) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    s[0] += ts[u][0];
+                    s[1] += ts[u][1];
+                }
+            } else {
+                // rare (wave-uniform branch): redo this stage exactly in the
+                // lanes whose tile sums left the fixed reference's range
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (ok) {
+                        s[0] += ts[u][0];
+                        s[1] += ts[u][1];
+                    } else {
+                        exact_update(acc[u][0], c2, false, 0, 0, lane, m[0], s[0]);
+                        exact_update(acc[u][1], c2, false, 0, 0, lane, m[1], s[1]);
+                    }
+                }
+            }
         }
+        if (si + 1 < ns) {
+            st.store(tid, smem + ((si + 1) & 1) * (KS * PITCH));
+            if (si + 2 < ns) st.load(tid, Kg, key0(si + 2), n, kstride);
+        }
+        __syncthreads();
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const float tot = sum[t] + __shfl_xor(sum[t], 32, 64);
-        const int64_t i = q0 + 32 * t + (lane & 31);
-        if (lane < 32 && i < n) lse[(int64_t)h * n + i] = (m[t] + __log2f(tot)) * kLn2;
+        const float mo = __shfl_xor(m[t], 32, 64);
+        const float so = __shfl_xor(s[t], 32, 64);
+        const float M = fmaxf(m[t], mo);
+        const float tot = ((m[t] == -INFINITY) ? 0.0f : s[t] * ex2(m[t] - M)) +
+                          ((mo == -INFINITY) ? 0.0f : so * ex2(mo - M));
+        const int64_t i = q0 + 32 * t + col;
+        if (lane < 32 && i < n) lse2[(int64_t)h * n + i] = M + log2f(tot);
     }
 }
 
 // ---------------------------------------------------------------- pass 2 --
-template <int D, int W>
-__global__ __launch_bounds__(W * 64) void colsum_kernel(
+// The 16 per-row values of the C-tile rows held by `lane` (rows crow(e, lane))
+// from a 32-entry LDS vector.
+__device__ __forceinline__ void load_rows(const float* v32, int lane, float (&L)[16]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const float4 v = *reinterpret_cast<const float4*>(v32 + 8 * b + 4 * (lane >> 5));
+        L[4 * b + 0] = v.x;
+        L[4 * b + 1] = v.y;
+        L[4 * b + 2] = v.z;
+        L[4 * b + 3] = v.w;
+    }
+}
+
+// Sum over the 16 elements of a pass-2 C tile of 2^(c2 x - L[e]).
+__device__ __forceinline__ float tile_colsum(const floatx16& a, const float (&L)[16], float c2) {
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+        s0 += ex2(fmaf(a[e + 0], c2, -L[e + 0]));
+        s1 += ex2(fmaf(a[e + 1], c2, -L[e + 1]));
+        s2 += ex2(fmaf(a[e + 2], c2, -L[e + 2]));
+        s3 += ex2(fmaf(a[e + 3], c2, -L[e + 3]));
+    }
+    return (s0 + s1) + (s2 + s3);
+}
+
+// Same on a diagonal tile: only rows (queries) at or after the lane's key.
+__device__ __forceinline__ float tile_colsum_masked(const floatx16& a, const float (&L)[16],
+                                                    float c2, int64_t it0, int64_t key,
+                                                    int lane) {
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float p = ex2(fmaf(a[e], c2, -L[e]));
+        s += (it0 + crow(e, lane) >= key) ? p : 0.0f;
+    }
+    return s;
+}
+
+template <int D, int KW, int QS>
+__global__ __launch_bounds__(KW * 64) void colsum_kernel(
     const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
-    const float* __restrict__ lse, float* __restrict__ partial, int64_t n, int64_t ldp,
-    int Hq, int Hkv, float c2) {
-    extern __shared__ _Float16 smem[];  // [W][32][D + 8], then float [W][64]
+    const float* __restrict__ lse2, float* __restrict__ partial, int64_t n, int64_t ldp, int Hq,
+    int Hkv, float c2) {
+    constexpr int NT = KW * 64;
     constexpr int C = D / 16;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int R = Hq / Hkv;
-    const int chunks = R / W;
-    const int g = blockIdx.x / chunks;
-    const int hbase = g * R + (blockIdx.x % chunks) * W;
-    const int h = hbase + wave;
-    const int64_t k0 = (int64_t)blockIdx.y * kKB;  // blockIdx.y = 0 has the most work
+    constexpr int PITCH = D + 8;
+    constexpr int U = QS / 32;  // 32-query units per stage
+    static_assert(QS <= NT, "one lse value per thread and stage");
+    extern __shared__ _Float16 smem[];  // [2][QS][PITCH], then float [2][QS]
+    float* lsm = reinterpret_cast<float*>(smem + 2 * QS * PITCH);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int khalf = 8 * (lane >> 5);
+    const int h = blockIdx.x;
+    const int g = h / (Hq / Hkv);
+    const int64_t K0 = (int64_t)blockIdx.y * (kColKeys * KW);  // blockIdx.y = 0: most work
+    const int64_t k0 = K0 + kColKeys * wave;
 
     // stationary key fragments (B operand of S = Q K^T)
     half8 kf[2][C];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int64_t j = k0 + 32 * t + (lane & 31);
+        const int64_t j = k0 + 32 * t + col;
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            kf[t][c] = (j < n) ? *reinterpret_cast<const half8*>(
-                                     K + (j * Hkv + g) * D + c * 16 + 8 * (lane >> 5))
+        for (int c = 0; c < C; ++c)
+            kf[t][c] = (j < n) ? *reinterpret_cast<const half8*>(K + (j * Hkv + g) * D + c * 16 +
+                                                                 khalf)
                                : zero8();
-        }
     }
 
-    Stager<D, W, W * 64> st;
-    const int tid = threadIdx.x;
-    const _Float16* Qg = Q + (int64_t)hbase * D;
+    const int ns = (int)((n - K0 + QS - 1) / QS);  // query stages from K0 on
+    Stager<D, QS, NT> st;
+    const _Float16* Qh = Q + (int64_t)h * D;
     const int64_t qstride = (int64_t)Hq * D;
-    const float* lrow = lse + (int64_t)h * n;
-
-    const int64_t it0 = k0 / 32;             // first query tile (diagonal of sub-tile 0)
-    const int64_t nit = (n + 31) / 32;       // query tiles it0 .. nit-1
-    float col[2] = {0.0f, 0.0f};
-
-    st.load(tid, Qg, it0 * 32, n, qstride);
-    const bool aligned4 = (((int64_t)h * n) & 3) == 0;
-    for (int64_t it = it0; it < nit; ++it) {
-        __syncthreads();
-        st.store(tid, smem);
-        __syncthreads();
-        if (it + 1 < nit) st.load(tid, Qg, (it + 1) * 32, n, qstride);
-
-        const int64_t i0 = it * 32;
-        // base-2 log-sum-exp of this lane's 16 rows
-        float L2[16];
-        const bool full = (i0 + 32 <= n) && aligned4;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int r = 8 * b + 4 * (lane >> 5);
-            if (full) {
-                const float4 v = *reinterpret_cast<const float4*>(lrow + i0 + r);
-                L2[4 * b + 0] = v.x * kLog2e;
-                L2[4 * b + 1] = v.y * kLog2e;
-                L2[4 * b + 2] = v.z * kLog2e;
-                L2[4 * b + 3] = v.w * kLog2e;
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    L2[4 * b + u] = (i0 + r + u < n) ? lrow[i0 + r + u] * kLog2e : INFINITY;
-            }
-        }
-        const bool need1 = (it > it0);  // sub-tile 1 keys start 32 after i0 of the first tile
-        floatx16 acc[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-        const _Float16* arow = smem + (wave * 32 + (lane & 31)) * (D + 8) + 8 * (lane >> 5);
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
-            acc[0] = mfma32(a, kf[0][c], acc[0]);
-            if (need1) acc[1] = mfma32(a, kf[1][c], acc[1]);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if (t == 1 && !need1) continue;
-            const int64_t j0 = k0 + 32 * t;
-            const bool diag = (i0 == j0);
-            const int jc = lane & 31;
-            float s = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float p = fast_exp2(fmaf(acc[t][e], c2, -L2[e]));
-                if (diag && crow(e, lane) < jc) p = 0.0f;
-                s += p;
-            }
-            col[t] += s;
-        }
+    const float* lrow = lse2 + (int64_t)h * n;
+    auto lload = [&](int s) -> float {
+        const int64_t i = K0 + (int64_t)QS * s + tid;
+        return (tid < QS && i < n) ? lrow[i] : INFINITY;  // no query: weight 2^-inf = 0
+    };
+    st.load(tid, Qh, K0, n, qstride);
+    float lv = lload(0);
+    st.store(tid, smem);
+    if (tid < QS) lsm[tid] = lv;
+    if (ns > 1) {
+        st.load(tid, Qh, K0 + QS, n, qstride);
+        lv = lload(1);
     }
-    // combine the two half-waves, then the W heads in a fixed order
-    float* red = reinterpret_cast<float*>(smem + (size_t)W * 32 * (D + 8));
     __syncthreads();
+
+    float cs[2] = {0.0f, 0.0f};
+    for (int si = 0; si < ns; ++si) {
+        const _Float16* buf = smem + (si & 1) * (QS * PITCH);
+        const float* lb = lsm + (si & 1) * QS;
+        const int64_t s0 = K0 + (int64_t)QS * si;
+        if (s0 >= k0 + kColKeys) {
+            // every query of the stage is after every key of this wavefront
+            floatx16 acc[U][2];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                acc[u][0] = zero16();
+                acc[u][1] = zero16();
+                const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
+                    acc[u][0] = mfma32(a, kf[0][c], acc[u][0]);
+                    acc[u][1] = mfma32(a, kf[1][c], acc[u][1]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float L[16];
+                load_rows(lb + 32 * u, lane, L);
+                cs[0] += tile_colsum(acc[u][0], L, c2);
+                cs[1] += tile_colsum(acc[u][1], L, c2);
+            }
+        } else if (s0 + QS > k0) {
+            // the stage crosses this wavefront's keys: causal mask
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t it0 = s0 + 32 * u;
+                const bool need0 = k0 <= it0 + 31;
+                const bool need1 = k0 + 32 <= it0 + 31;
+                if (!need0) continue;
+                float L[16];
+                load_rows(lb + 32 * u, lane, L);
+                floatx16 acc0 = zero16(), acc1 = zero16();
+                const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
+                    acc0 = mfma32(a, kf[0][c], acc0);
+                    if (need1) acc1 = mfma32(a, kf[1][c], acc1);
+                }
+                cs[0] += tile_colsum_masked(acc0, L, c2, it0, k0 + col, lane);
+                if (need1) cs[1] += tile_colsum_masked(acc1, L, c2, it0, k0 + 32 + col, lane);
+            }
+        }
+        if (si + 1 < ns) {
+            st.store(tid, smem + ((si + 1) & 1) * (QS * PITCH));
+            if (tid < QS) lsm[((si + 1) & 1) * QS + tid] = lv;
+            if (si + 2 < ns) {
+                st.load(tid, Qh, K0 + (int64_t)QS * (si + 2), n, qstride);
+                lv = lload(si + 2);
+            }
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const float v = col[t] + __shfl_xor(col[t], 32, 64);
-        if (lane < 32) red[wave * 64 + 32 * t + lane] = v;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        float v = 0.0f;
-        for (int w = 0; w < W; ++w) v += red[w * 64 + lane];
-        const int64_t j = k0 + lane;
-        if (j < n) partial[(int64_t)(blockIdx.x) * ldp + j] = v;
+        const float v = cs[t] + __shfl_xor(cs[t], 32, 64);
+        const int64_t j = k0 + 32 * t + col;
+        if (lane < 32 && j < n) partial[(int64_t)h * ldp + j] = v;
     }
 }
 
@@ -326,95 +490,95 @@ __global__ void reduce_kernel(const float* __restrict__ partial, int64_t ldp, in
     score[j] = acc ? score[j] + v : v;
 }
 
-// Heads per workgroup: the largest divisor of R = Hq/Hkv that keeps the
-// workgroup within 8 wavefronts (4 for d = 256) and the pass's LDS staging
-// within 64 KiB.
-int heads_per_wg(int R, int D, bool pass2) {
-    for (int w = kMaxWaves; w >= 1; --w) {
-        if (R % w) continue;
-        if (D == 256 && w > 4) continue;  // register budget of the d=256 fragments
-        const size_t lds = pass2 ? (size_t)w * 32 * (D + 8) * 2 + (size_t)w * 64 * 4
-                                 : (size_t)32 * (D + 8) * 2;
-        if (lds <= 64 * 1024) return w;
-    }
+// Pass-1 workgroup shape: W heads of a GQA group (the largest divisor of
+// R = Hq/Hkv up to 8) times QW blocks of 64 queries, about 4 wavefronts.
+int rowlse_heads(int R) {
+    for (int w = 8; w >= 1; --w)
+        if (R % w == 0) return w;
     return 1;
 }
 
-template <typename F>
-hipError_t dispatch_dw(int d, int w, F&& f) {
-#define SK_W_CASES(DV)                                                   \
-    switch (w) {                                                         \
-        case 1: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 1>{}); \
-        case 2: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 2>{}); \
-        case 3: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 3>{}); \
-        case 4: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 4>{}); \
-        case 5: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 5>{}); \
-        case 6: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 6>{}); \
-        case 7: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 7>{}); \
-        case 8: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 8>{}); \
-        default: return hipErrorInvalidValue;                            \
-    }
-    switch (d) {
-        case 64: SK_W_CASES(64)
-        case 128: SK_W_CASES(128)
-        case 256: SK_W_CASES(256)
+constexpr int rowlse_qblocks(int W) { return W >= 3 ? 1 : 4 / W; }
+
+template <int D>
+constexpr int stage_rows() { return D == 256 ? 32 : kStageKeys; }
+
+template <int D, int W>
+hipError_t launch_rowlse_t(const Dims& s, const void* q, const void* k, float* lse2,
+                           hipStream_t st) {
+    constexpr int QW = rowlse_qblocks(W);
+    constexpr int KS = stage_rows<D>();
+    const int64_t QB = 64 * QW;
+    const dim3 grid((unsigned)(s.Hq / W), (unsigned)((s.n + QB - 1) / QB));
+    const float c2 = kLog2e / sqrtf((float)s.d);
+    const size_t lds = (size_t)2 * KS * (D + 8) * 2;
+    hipLaunchKernelGGL((rowlse_kernel<D, W, QW, KS>), grid, dim3(W * QW * 64), lds, st,
+                       (const _Float16*)q, (const _Float16*)k, lse2, s.n, s.Hq, s.Hkv, c2);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_rowlse_d(const Dims& s, const void* q, const void* k, float* lse2,
+                           hipStream_t st) {
+    switch (rowlse_heads(s.Hq / s.Hkv)) {
+        case 1: return launch_rowlse_t<D, 1>(s, q, k, lse2, st);
+        case 2: return launch_rowlse_t<D, 2>(s, q, k, lse2, st);
+        case 3: return launch_rowlse_t<D, 3>(s, q, k, lse2, st);
+        case 4: return launch_rowlse_t<D, 4>(s, q, k, lse2, st);
+        case 5: return launch_rowlse_t<D, 5>(s, q, k, lse2, st);
+        case 6: return launch_rowlse_t<D, 6>(s, q, k, lse2, st);
+        case 7: return launch_rowlse_t<D, 7>(s, q, k, lse2, st);
+        case 8: return launch_rowlse_t<D, 8>(s, q, k, lse2, st);
         default: return hipErrorInvalidValue;
     }
-#undef SK_W_CASES
+}
+
+template <int D>
+hipError_t launch_colsum_d(const Dims& s, const void* q, const void* k, const float* lse2,
+                           float* partial, hipStream_t st) {
+    constexpr int QS = stage_rows<D>();
+    const int64_t KB = (int64_t)kColKeys * kColWaves;
+    const dim3 grid((unsigned)s.Hq, (unsigned)((s.n + KB - 1) / KB));
+    const float c2 = kLog2e / sqrtf((float)s.d);
+    const size_t lds = (size_t)2 * QS * (D + 8) * 2 + (size_t)2 * QS * 4;
+    hipLaunchKernelGGL((colsum_kernel<D, kColWaves, QS>), grid, dim3(kColWaves * 64), lds, st,
+                       (const _Float16*)q, (const _Float16*)k, lse2, partial, s.n,
+                       padded_tokens(s.n), s.Hq, s.Hkv, c2);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t padded_tokens(int64_t n) { return (n + kKB - 1) / kKB * kKB; }
+int64_t padded_tokens(int64_t n) { return (n + kColKeys - 1) / kColKeys * kColKeys; }
 
-hipError_t launch_rowlse(const Dims& s, const void* q, const void* k, float* lse,
+hipError_t launch_rowlse(const Dims& s, const void* q, const void* k, float* lse2,
                          hipStream_t st) {
-    const int R = s.Hq / s.Hkv;
-    const int W = heads_per_wg(R, s.d, false);
-    const dim3 grid((unsigned)(s.Hq / W), (unsigned)((s.n + kQB - 1) / kQB));
-    const float c2 = kLog2e / sqrtf((float)s.d);
-    return dispatch_dw(s.d, W, [&](auto Dc, auto Wc) {
-        constexpr int D = decltype(Dc)::value;
-        constexpr int WW = decltype(Wc)::value;
-        const size_t lds = (size_t)32 * (D + 8) * 2;
-        hipLaunchKernelGGL((rowlse_kernel<D, WW>), grid, dim3(WW * 64), lds, st,
-                           (const _Float16*)q, (const _Float16*)k, lse, s.n, s.Hq, s.Hkv, c2);
-        return hipGetLastError();
-    });
+    switch (s.d) {
+        case 64: return launch_rowlse_d<64>(s, q, k, lse2, st);
+        case 128: return launch_rowlse_d<128>(s, q, k, lse2, st);
+        case 256: return launch_rowlse_d<256>(s, q, k, lse2, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_colsum(const Dims& s, const void* q, const void* k, const float* lse,
+hipError_t launch_colsum(const Dims& s, const void* q, const void* k, const float* lse2,
                          float* partial, hipStream_t st) {
-    const int R = s.Hq / s.Hkv;
-    const int W = heads_per_wg(R, s.d, true);
-    const dim3 grid((unsigned)(s.Hq / W), (unsigned)((s.n + kKB - 1) / kKB));
-    const float c2 = kLog2e / sqrtf((float)s.d);
-    const int64_t ldp = padded_tokens(s.n);
-    return dispatch_dw(s.d, W, [&](auto Dc, auto Wc) {
-        constexpr int D = decltype(Dc)::value;
-        constexpr int WW = decltype(Wc)::value;
-        const size_t lds = (size_t)WW * 32 * (D + 8) * 2 + (size_t)WW * 64 * 4;
-        hipLaunchKernelGGL((colsum_kernel<D, WW>), grid, dim3(WW * 64), lds, st,
-                           (const _Float16*)q, (const _Float16*)k, lse, partial, s.n, ldp,
-                           s.Hq, s.Hkv, c2);
-        return hipGetLastError();
-    });
+    switch (s.d) {
+        case 64: return launch_colsum_d<64>(s, q, k, lse2, partial, st);
+        case 128: return launch_colsum_d<128>(s, q, k, lse2, partial, st);
+        case 256: return launch_colsum_d<256>(s, q, k, lse2, partial, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_reduce(const Dims& s, const float* partial, float* score, int acc,
                          hipStream_t st) {
-    const int R = s.Hq / s.Hkv;
-    const int W = heads_per_wg(R, s.d, true);
-    const int P = s.Hq / W;
-    const int64_t ldp = padded_tokens(s.n);
     const unsigned blocks = (unsigned)((s.n + 255) / 256);
-    hipLaunchKernelGGL(reduce_kernel, dim3(blocks), dim3(256), 0, st, partial, ldp, P, s.n,
-                       score, acc);
+    hipLaunchKernelGGL(reduce_kernel, dim3(blocks), dim3(256), 0, st, partial,
+                       padded_tokens(s.n), s.Hq, s.n, score, acc);
     return hipGetLastError();
 }
 
-int colsum_partial_rows(const Dims& s) {
-    return s.Hq / heads_per_wg(s.Hq / s.Hkv, s.d, true);
-}
+int colsum_partial_rows(const Dims& s) { return s.Hq; }
 
 }  // namespace sk

@@ -16,6 +16,7 @@ from tests.gpu_helpers import Guarded, say, to_dev
 pytestmark = pytest.mark.gpu
 
 RTOL = 2e-3
+LOG2E = 1.0 / np.log(2.0)   # sk_score_rowlse reports the log-sum-exp in base 2
 
 
 def _rand(seed, n, Hq, Hkv, d, scale=1.0):
@@ -89,7 +90,7 @@ def test_rowlse_and_colsum_entry_points():
     torch.cuda.synchronize()
     lse_h = lse.cpu().numpy().astype(np.float64)
     for h in (0, 3, 7):
-        want = OS.head_row_lse(q[:, h, :], k[:, h // 4, :])
+        want = OS.head_row_lse(q[:, h, :], k[:, h // 4, :]) * LOG2E
         assert np.max(np.abs(lse_h[h] - want)) < 1e-3
     _close(out.cpu().numpy().astype(np.float64), OS.layer_score(q, k), "colsum")
     # odd n makes the per-head lse rows misaligned for vector loads
@@ -139,8 +140,30 @@ def test_full_size_sampled(name):
     rows = np.sort(rng.integers(0, n, 24))
     lse_h = lse.cpu().numpy().astype(np.float64)
     for h in (0, Hq - 1):
-        want = OS.head_row_lse(q[:, h, :], k[:, h // (Hq // Hkv), :], rows)
+        want = OS.head_row_lse(q[:, h, :], k[:, h // (Hq // Hkv), :], rows) * LOG2E
         assert np.max(np.abs(lse_h[h, rows] - want)) < 1e-3
     cols = np.unique(np.concatenate([np.arange(n - 40, n), rng.integers(n - 1024, n, 24)]))
     say("oracle sampled columns", len(cols))
     _close(got[cols], OS.layer_column_sample(q, k, cols), name)
+
+
+@pytest.mark.parametrize("boost", [30.0, 50.0, 80.0])
+def test_logit_far_above_diagonal_reference(boost):
+    """Key 0 carries a logit `boost` (natural units) above every other logit
+    of each row.  Pass 1 takes its per-row reference from the diagonal keys,
+    so for rows beyond the first key stage this exercises the exp2 range of
+    the fixed-reference sums (30, i.e. 43 in base 2) and the exact fallback
+    past 2^64 (50 and 80, i.e. 72 and 115 in base 2).  The other tokens'
+    scores are then about e^-boost, which stays in fp32's normal range."""
+    n, Hq, Hkv, d = 700, 8, 2, 128
+    r = np.random.default_rng(40)
+    q = (r.standard_normal((n, Hq, d)) * 0.3).astype(np.float32)
+    k = (r.standard_normal((n, Hkv, d)) * 0.3).astype(np.float32)
+    q[:, :, 0] = 4.0
+    k[:, :, 0] = 0.0
+    k[0, :, 0] = boost * np.sqrt(d) / 4.0
+    q, k = q.astype(np.float16), k.astype(np.float16)
+    say("score boost", boost)
+    _, got = _gpu(q, k)
+    _close(got, OS.layer_score(q, k), f"boost {boost}")
+    assert abs(got.sum() - Hq * n) <= 1e-4 * Hq * n
