@@ -95,43 +95,57 @@ __device__ __forceinline__ int crow(int e, int lane) {
     return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
 }
 
+// Buffer resource over `bytes` bytes at `base` for raw loads: the hardware
+// range check returns zeros for any load at or past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
 // Cooperative staging of ROWS tokens x D halfs (contiguous per token in
 // global memory, token stride `gstride` halfs) into LDS rows of D + 8 halfs
-// by NT threads, through registers so that the global loads of the next
-// stage are in flight while the current one is computed on.  The row pitch
-// of D + 8 halfs puts the 32 rows of an MFMA fragment read at distinct
-// bank groups.  Tokens at or beyond n are stored as zeros.
+// by NT threads, through registers, so that the loads of the next stage are
+// in flight while the current one is computed on.  The row pitch of D + 8
+// halfs puts the 32 rows of an MFMA fragment read at distinct bank groups.
+// Each thread owns the same 16-byte pieces in every stage: its first piece
+// at a fixed per-thread offset, the others a uniform number of rows further
+// (an SGPR offset for the buffer load, an immediate for the LDS store).  The
+// stage's buffer resource covers only its tokens below n, so the range check
+// zero-fills the ragged tail.
 template <int D, int ROWS, int NT>
 struct Stager {
-    static constexpr int kPieces = D / 8;  // 16-byte pieces per row
-    static constexpr int kTotal = ROWS * kPieces;
-    static constexpr int kRegs = (kTotal + NT - 1) / NT;
+    static constexpr int kPieces = D / 8;           // 16-byte pieces per row
+    static constexpr int kRowStep = NT / kPieces;   // rows between a thread's pieces
+    static constexpr int kRegs = (ROWS + kRowStep - 1) / kRowStep;
+    static_assert(NT % kPieces == 0, "whole rows per thread step");
     uint4 regs[kRegs];
-    __device__ __forceinline__ void load(int tid, const _Float16* __restrict__ g, int64_t t0,
-                                         int64_t n, int64_t gstride) {
+    uint32_t voff;  // byte offset of this thread's first piece within a stage
+    int row0;       // its row within the stage
+    int loff;       // its LDS offset (halfs) within a stage buffer
+    __device__ __forceinline__ void init(int tid, int64_t gstride) {
+        row0 = tid / kPieces;
+        const int piece = tid % kPieces;
+        voff = (uint32_t)((row0 * gstride + piece * 8) * 2);
+        loff = row0 * (D + 8) + piece * 8;
+    }
+    // g points at token t0 of this head's rows; n_left = n - t0 > 0.
+    __device__ __forceinline__ void load(const _Float16* g, int64_t n_left, int64_t gstride) {
+        const int64_t rows = n_left < ROWS ? n_left : ROWS;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(g, (uint32_t)(rows * gstride * 2));
 #pragma unroll
         for (int r = 0; r < kRegs; ++r) {
-            const int idx = tid + r * NT;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (kTotal % NT == 0 || idx < kTotal) {
-                const int tok = idx / kPieces;
-                const int piece = idx % kPieces;
-                if (t0 + tok < n)
-                    v = *reinterpret_cast<const uint4*>(g + (t0 + tok) * gstride + piece * 8);
+            if (ROWS % kRowStep == 0 || row0 + r * kRowStep < ROWS) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, voff, (int)(r * kRowStep * gstride * 2), 0);
+                regs[r] = *reinterpret_cast<const uint4*>(&v);
             }
-            regs[r] = v;
         }
     }
-    __device__ __forceinline__ void store(int tid, _Float16* lds) const {
+    __device__ __forceinline__ void store(_Float16* lds) const {
 #pragma unroll
-        for (int r = 0; r < kRegs; ++r) {
-            const int idx = tid + r * NT;
-            if (kTotal % NT == 0 || idx < kTotal) {
-                const int tok = idx / kPieces;
-                const int piece = idx % kPieces;
-                *reinterpret_cast<uint4*>(lds + tok * (D + 8) + piece * 8) = regs[r];
-            }
-        }
+        for (int r = 0; r < kRegs; ++r)
+            if (ROWS % kRowStep == 0 || row0 + r * kRowStep < ROWS)
+                *reinterpret_cast<uint4*>(lds + loff + r * kRowStep * (D + 8)) = regs[r];
     }
 };
 
@@ -172,9 +186,29 @@ __device__ __forceinline__ void exact_update(const floatx16& a, float c2, bool m
     m = mn;
 }
 
+// Fixed-reference update of one lane's two row sums with one 32-key unit
+// (two C tiles): add 2^(c2 x - m); if a tile sum leaves [0, 2^64] in any lane
+// (a logit far above the reference), that lane redoes the unit exactly.
+__device__ __forceinline__ void fixed_ref_update(const floatx16 (&a)[2], float c2, int lane,
+                                                 float (&m)[2], float (&s)[2]) {
+    const float t0 = tile_expsum(a[0], c2, m[0]);
+    const float t1 = tile_expsum(a[1], c2, m[1]);
+    const bool ok = (t0 <= kTileLimit) && (t1 <= kTileLimit);
+    if (__builtin_expect(__all(ok), 1)) {
+        s[0] += t0;
+        s[1] += t1;
+    } else if (ok) {
+        s[0] += t0;
+        s[1] += t1;
+    } else {
+        exact_update(a[0], c2, false, 0, 0, lane, m[0], s[0]);
+        exact_update(a[1], c2, false, 0, 0, lane, m[1], s[1]);
+    }
+}
+
 // ---------------------------------------------------------------- pass 1 --
 template <int D, int W, int QW, int KS>
-__global__ __launch_bounds__(W * QW * 64) void rowlse_kernel(
+__global__ __launch_bounds__(W * QW * 64, D == 256 ? 1 : 2) void rowlse_kernel(
     const _Float16* __restrict__ Q, const _Float16* __restrict__ K, float* __restrict__ lse2,
     int64_t n, int Hq, int Hkv, float c2) {
     constexpr int NT = W * QW * 64;
@@ -218,97 +252,84 @@ __global__ __launch_bounds__(W * QW * 64) void rowlse_kernel(
     Stager<D, KS, NT> st;
     const _Float16* Kg = K + (int64_t)g * D;
     const int64_t kstride = (int64_t)Hkv * D;
-    st.load(tid, Kg, key0(0), n, kstride);
-    st.store(tid, smem);
-    if (ns > 1) st.load(tid, Kg, key0(1), n, kstride);
+    auto kload = [&](int s) { st.load(Kg + key0(s) * kstride, n - key0(s), kstride); };
+    st.init(tid, kstride);
+    kload(0);
+    st.store(smem);
+    if (ns > 1) kload(1);
     __syncthreads();
 
     float m[2] = {-INFINITY, -INFINITY};
     float s[2] = {0.0f, 0.0f};
-    for (int si = 0; si < ns; ++si) {
-        const _Float16* buf = smem + (si & 1) * (KS * PITCH);
-        const int64_t k0 = key0(si);
-        if (si < nd) {
-            // diagonal stages: masked, exact online max
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t kt0 = k0 + 32 * u;
-                const bool need0 = kt0 <= q0 + 31;
-                const bool need1 = kt0 <= q0 + 63;
-                if (!need1) continue;
-                floatx16 acc0 = zero16(), acc1 = zero16();
-                const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
-                    if (need0) acc0 = mfma32(a, qf[0][c], acc0);
-                    acc1 = mfma32(a, qf[1][c], acc1);
-                }
-                if (need0)
-                    exact_update(acc0, c2, kt0 + 31 > q0, kt0, q0 + col, lane, m[0], s[0]);
-                exact_update(acc1, c2, kt0 + 31 > q0 + 32, kt0, q0 + 32 + col, lane, m[1], s[1]);
-            }
-            if (si == nd - 1) {
-                // one reference per query row for the fast stages
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    float mn = fmaxf(m[t], __shfl_xor(m[t], 32, 64));
-                    if (mn == -INFINITY) mn = 0.0f;
-                    s[t] = (m[t] == -INFINITY) ? 0.0f : s[t] * ex2(m[t] - mn);
-                    m[t] = mn;
-                }
-            }
-        } else {
-            // stages strictly below the diagonal: no mask, fixed reference
-            floatx16 acc[U][2];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                acc[u][0] = zero16();
-                acc[u][1] = zero16();
-                const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
-                    acc[u][0] = mfma32(a, qf[0][c], acc[u][0]);
-                    acc[u][1] = mfma32(a, qf[1][c], acc[u][1]);
-                }
-            }
-            float ts[U][2];
-            bool ok = true;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    ts[u][t] = tile_expsum(acc[u][t], c2, m[t]);
-                    ok = ok && (ts[u][t] <= kTileLimit);
-                }
-            if (__builtin_expect(__all(ok), 1)) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    s[0] += ts[u][0];
-                    s[1] += ts[u][1];
-                }
-            } else {
-                // rare (wave-uniform branch): redo this stage exactly in the
-                // lanes whose tile sums left the fixed reference's range
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (ok) {
-                        s[0] += ts[u][0];
-                        s[1] += ts[u][1];
-                    } else {
-                        exact_update(acc[u][0], c2, false, 0, 0, lane, m[0], s[0]);
-                        exact_update(acc[u][1], c2, false, 0, 0, lane, m[1], s[1]);
-                    }
-                }
-            }
-        }
+    auto next_stage = [&](int si) {
         if (si + 1 < ns) {
-            st.store(tid, smem + ((si + 1) & 1) * (KS * PITCH));
-            if (si + 2 < ns) st.load(tid, Kg, key0(si + 2), n, kstride);
+            st.store(smem + ((si + 1) & 1) * (KS * PITCH));
+            if (si + 2 < ns) kload(si + 2);
         }
         __syncthreads();
+    };
+
+    // diagonal stages: causal mask, exact online max
+    for (int si = 0; si < nd; ++si) {
+        const _Float16* buf = smem + (si & 1) * (KS * PITCH);
+        const int64_t k0 = key0(si);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kt0 = k0 + 32 * u;
+            const bool need0 = kt0 <= q0 + 31;
+            const bool need1 = kt0 <= q0 + 63;
+            if (!need1) continue;
+            floatx16 acc0 = zero16(), acc1 = zero16();
+            const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
+                if (need0) acc0 = mfma32(a, qf[0][c], acc0);
+                acc1 = mfma32(a, qf[1][c], acc1);
+            }
+            if (need0) exact_update(acc0, c2, kt0 + 31 > q0, kt0, q0 + col, lane, m[0], s[0]);
+            exact_update(acc1, c2, kt0 + 31 > q0 + 32, kt0, q0 + 32 + col, lane, m[1], s[1]);
+        }
+        next_stage(si);
     }
+    // one reference per query row for the remaining stages
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float mn = fmaxf(m[t], __shfl_xor(m[t], 32, 64));
+        if (mn == -INFINITY) mn = 0.0f;
+        s[t] = (m[t] == -INFINITY) ? 0.0f : s[t] * ex2(m[t] - mn);
+        m[t] = mn;
+    }
+
+    // stages strictly below the diagonal: no mask, fixed reference.  The
+    // pipeline runs the softmax of each 32-key unit while the MFMAs of the
+    // next unit (in this stage or the next) execute; `pend` starts as -inf,
+    // which contributes exactly zero.
+    floatx16 pend[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        pend[0][e] = -INFINITY;
+        pend[1][e] = -INFINITY;
+    }
+    for (int si = nd; si < ns; ++si) {
+        const _Float16* buf = smem + (si & 1) * (KS * PITCH);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            floatx16 cur0 = zero16(), cur1 = zero16();
+            const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
+                cur0 = mfma32(a, qf[0][c], cur0);
+                cur1 = mfma32(a, qf[1][c], cur1);
+            }
+            fixed_ref_update(pend, c2, lane, m, s);
+            pend[0] = cur0;
+            pend[1] = cur1;
+        }
+        next_stage(si);
+    }
+    fixed_ref_update(pend, c2, lane, m, s);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const float mo = __shfl_xor(m[t], 32, 64);
@@ -362,7 +383,7 @@ __device__ __forceinline__ float tile_colsum_masked(const floatx16& a, const flo
 }
 
 template <int D, int KW, int QS>
-__global__ __launch_bounds__(KW * 64) void colsum_kernel(
+__global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
     const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     const float* __restrict__ lse2, float* __restrict__ partial, int64_t n, int64_t ldp, int Hq,
     int Hkv, float c2) {
@@ -371,7 +392,9 @@ __global__ __launch_bounds__(KW * 64) void colsum_kernel(
     constexpr int PITCH = D + 8;
     constexpr int U = QS / 32;  // 32-query units per stage
     static_assert(QS <= NT, "one lse value per thread and stage");
-    extern __shared__ _Float16 smem[];  // [2][QS][PITCH], then float [2][QS]
+    // [2][QS][PITCH] query tiles, then float [3][QS] lse values: the pipeline
+    // reads a stage's lse values one stage after its query tile
+    extern __shared__ _Float16 smem[];
     float* lsm = reinterpret_cast<float*>(smem + 2 * QS * PITCH);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -404,45 +427,62 @@ __global__ __launch_bounds__(KW * 64) void colsum_kernel(
         const int64_t i = K0 + (int64_t)QS * s + tid;
         return (tid < QS && i < n) ? lrow[i] : INFINITY;  // no query: weight 2^-inf = 0
     };
-    st.load(tid, Qh, K0, n, qstride);
+    auto qload = [&](int s) {
+        const int64_t t0 = K0 + (int64_t)QS * s;
+        st.load(Qh + t0 * qstride, n - t0, qstride);
+    };
+    st.init(tid, qstride);
+    qload(0);
     float lv = lload(0);
-    st.store(tid, smem);
+    st.store(smem);
     if (tid < QS) lsm[tid] = lv;
     if (ns > 1) {
-        st.load(tid, Qh, K0 + QS, n, qstride);
+        qload(1);
         lv = lload(1);
     }
     __syncthreads();
 
     float cs[2] = {0.0f, 0.0f};
+    // Software pipeline over the stages after this wavefront's keys: the
+    // column sums of each 32-query unit run while the MFMAs of the next unit
+    // execute.  `pend` starts as -inf with finite row values, which
+    // contributes exactly zero.
+    floatx16 pend[2];
+    const float* pL = lsm;  // finite or +inf values (the first stage's)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        pend[0][e] = -INFINITY;
+        pend[1][e] = -INFINITY;
+    }
     for (int si = 0; si < ns; ++si) {
         const _Float16* buf = smem + (si & 1) * (QS * PITCH);
-        const float* lb = lsm + (si & 1) * QS;
+        const float* lb = lsm + (si % 3) * QS;
         const int64_t s0 = K0 + (int64_t)QS * si;
         if (s0 >= k0 + kColKeys) {
             // every query of the stage is after every key of this wavefront
-            floatx16 acc[U][2];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                acc[u][0] = zero16();
-                acc[u][1] = zero16();
+                floatx16 cur0 = zero16(), cur1 = zero16();
                 const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
-                    acc[u][0] = mfma32(a, kf[0][c], acc[u][0]);
-                    acc[u][1] = mfma32(a, kf[1][c], acc[u][1]);
+                    cur0 = mfma32(a, kf[0][c], cur0);
+                    cur1 = mfma32(a, kf[1][c], cur1);
                 }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float L[16];
-                load_rows(lb + 32 * u, lane, L);
-                cs[0] += tile_colsum(acc[u][0], L, c2);
-                cs[1] += tile_colsum(acc[u][1], L, c2);
+                {
+                    float L[16];
+                    load_rows(pL, lane, L);
+                    cs[0] += tile_colsum(pend[0], L, c2);
+                    cs[1] += tile_colsum(pend[1], L, c2);
+                }
+                pend[0] = cur0;
+                pend[1] = cur1;
+                pL = lb + 32 * u;
             }
         } else if (s0 + QS > k0) {
-            // the stage crosses this wavefront's keys: causal mask
+            // the stage crosses this wavefront's keys: causal mask (these
+            // stages precede every full one, so nothing is pending yet)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t it0 = s0 + 32 * u;
@@ -464,14 +504,20 @@ __global__ __launch_bounds__(KW * 64) void colsum_kernel(
             }
         }
         if (si + 1 < ns) {
-            st.store(tid, smem + ((si + 1) & 1) * (QS * PITCH));
-            if (tid < QS) lsm[((si + 1) & 1) * QS + tid] = lv;
+            st.store(smem + ((si + 1) & 1) * (QS * PITCH));
+            if (tid < QS) lsm[((si + 1) % 3) * QS + tid] = lv;
             if (si + 2 < ns) {
-                st.load(tid, Qh, K0 + (int64_t)QS * (si + 2), n, qstride);
+                qload(si + 2);
                 lv = lload(si + 2);
             }
         }
         __syncthreads();
+    }
+    {
+        float L[16];
+        load_rows(pL, lane, L);
+        cs[0] += tile_colsum(pend[0], L, c2);
+        cs[1] += tile_colsum(pend[1], L, c2);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -540,7 +586,7 @@ hipError_t launch_colsum_d(const Dims& s, const void* q, const void* k, const fl
     const int64_t KB = (int64_t)kColKeys * kColWaves;
     const dim3 grid((unsigned)s.Hq, (unsigned)((s.n + KB - 1) / KB));
     const float c2 = kLog2e / sqrtf((float)s.d);
-    const size_t lds = (size_t)2 * QS * (D + 8) * 2 + (size_t)2 * QS * 4;
+    const size_t lds = (size_t)2 * QS * (D + 8) * 2 + (size_t)3 * QS * 4;
     hipLaunchKernelGGL((colsum_kernel<D, kColWaves, QS>), grid, dim3(kColWaves * 64), lds, st,
                        (const _Float16*)q, (const _Float16*)k, lse2, partial, s.n,
                        padded_tokens(s.n), s.Hq, s.Hkv, c2);
