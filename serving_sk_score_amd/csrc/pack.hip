@@ -82,15 +82,68 @@ __device__ __forceinline__ void quant8(const float (&x)[8], float a, int (&q)[8]
     }
 }
 
-template <int D>
+// One lane's 8 elements of a row (a 16-byte piece of fp16) quantized against
+// the absmax of the whole row, taken over the row's LPR lanes.
+template <int QMAX, int LPR>
+__device__ __forceinline__ void quant_piece(const uint4 raw, int (&q)[8], uint32_t& sbits) {
+    float x[8];
+    x[0] = h2f(raw.x);
+    x[1] = h2f(raw.x >> 16);
+    x[2] = h2f(raw.y);
+    x[3] = h2f(raw.y >> 16);
+    x[4] = h2f(raw.z);
+    x[5] = h2f(raw.z >> 16);
+    x[6] = h2f(raw.w);
+    x[7] = h2f(raw.w >> 16);
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
+    a = group_max<LPR>(a);
+    quant8<QMAX>(x, a, q, sbits);
+}
+
+// Rows of one (layer, token) handled per wavefront step: a row of D fp16
+// values is spread over D/8 lanes (one 16-byte piece each), so a step covers
+// 64/(D/8) rows.  A wavefront first issues the loads of NB steps (NB, a power
+// of two up to 8, covers all 2H rows of the token when it can), then
+// quantizes and stores them, so the loads of a token are in flight together.
+// Rows past the token's last one (a partial last batch) re-load that last
+// row and are not stored: the loads need no branches.
+constexpr int kMaxBatch = 8;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld_nt(const uint16_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(uint4 v, void* p) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st_nt(uint2 v, void* p) {
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_nt(uint32_t v, void* p) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+
+// Token index of this wavefront, made wave-uniform so that its map entry
+// (and block-table entry) are scalar loads.
+__device__ __forceinline__ int64_t wave_token() {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    return (int64_t)blockIdx.x * kWaves + w;
+}
+
+template <int D, int NB>
 __global__ __launch_bounds__(kWaves * 64) void pack_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint32_t* __restrict__ map, uint8_t* __restrict__ out, Segs sg, int64_t n,
     int H) {
-    constexpr int LPR = D / 8;    // lanes per row
-    constexpr int RPP = 64 / LPR; // rows per step
+    constexpr int LPR = D / 8;     // lanes per row
+    constexpr int RPP = 64 / LPR;  // rows per step
     const int lane = threadIdx.x & 63;
-    const int64_t j = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t j = wave_token();
     const int64_t layer = blockIdx.y;
     if (j >= n) return;
     const uint32_t m = map[j];
@@ -102,48 +155,64 @@ __global__ __launch_bounds__(kWaves * 64) void pack_kernel(
     const int64_t rowbase = (layer * sg.cnt[t] + slot) * rows;
     const int64_t tokrow = (layer * n + j) * H;
 
-    for (int r0 = 0; r0 < rows; r0 += RPP) {
-        const int r = r0 + lane / LPR;
-        if (r >= rows) break;  // whole row-groups leave together
-        const uint16_t* src = (r < H ? K : V) + (tokrow + (r < H ? r : r - H)) * D + part * 8;
-        const uint4 raw = *reinterpret_cast<const uint4*>(src);
-        const int64_t row = rowbase + r;
+    for (int b0 = 0; b0 < rows; b0 += NB * RPP) {
+        uint4 raw[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int r = min(b0 + i * RPP + lane / LPR, rows - 1);
+            const uint16_t* src = (r < H ? K : V) + (tokrow + (r < H ? r : r - H)) * D + part * 8;
+            raw[i] = ld_nt(src);
+        }
+        // the tier is uniform across the wavefront
         if (t == 0u) {
-            *reinterpret_cast<uint4*>(out + sg.oc[0] + row * (2 * D) + part * 16) = raw;
-            continue;
-        }
-        float x[8];
-        x[0] = h2f(raw.x);
-        x[1] = h2f(raw.x >> 16);
-        x[2] = h2f(raw.y);
-        x[3] = h2f(raw.y >> 16);
-        x[4] = h2f(raw.z);
-        x[5] = h2f(raw.z >> 16);
-        x[6] = h2f(raw.w);
-        x[7] = h2f(raw.w >> 16);
-        float a = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
-        a = group_max<LPR>(a);
-        int q[8];
-        uint32_t sbits;
-        if (t == 1u) {
-            quant8<127>(x, a, q, sbits);
-            uint2 w;
-            w.x = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) |
-                  ((uint32_t)(q[3] & 0xFF) << 24);
-            w.y = (q[4] & 0xFF) | ((q[5] & 0xFF) << 8) | ((q[6] & 0xFF) << 16) |
-                  ((uint32_t)(q[7] & 0xFF) << 24);
-            *reinterpret_cast<uint2*>(out + sg.oc[1] + row * D + part * 8) = w;
+            for (int i = 0; i < NB; ++i) {
+                const int r = b0 + i * RPP + lane / LPR;
+                if (r < rows) st_nt(raw[i], out + sg.oc[0] + (rowbase + r) * (2 * D) + part * 16);
+            }
+        } else if (t == 1u) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int r = b0 + i * RPP + lane / LPR;
+                if (b0 + i * RPP < rows) {  // whole steps: the row group's lanes together
+                    int q[8];
+                    uint32_t sbits;
+                    quant_piece<127, LPR>(raw[i], q, sbits);
+                    uint2 w;
+                    w.x = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) |
+                          ((uint32_t)(q[3] & 0xFF) << 24);
+                    w.y = (q[4] & 0xFF) | ((q[5] & 0xFF) << 8) | ((q[6] & 0xFF) << 16) |
+                          ((uint32_t)(q[7] & 0xFF) << 24);
+                    if (r < rows) {
+                        const int64_t row = rowbase + r;
+                        st_nt(w, out + sg.oc[1] + row * D + part * 8);
+                        if (part == 0)
+                            *reinterpret_cast<uint16_t*>(out + sg.os[1] + row * 2) =
+                                (uint16_t)sbits;
+                    }
+                }
+            }
         } else {
-            quant8<7>(x, a, q, sbits);
-            uint32_t w = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w |= (uint32_t)(q[e] & 0xF) << (4 * e);
-            *reinterpret_cast<uint32_t*>(out + sg.oc[2] + row * (D / 2) + part * 4) = w;
+            for (int i = 0; i < NB; ++i) {
+                const int r = b0 + i * RPP + lane / LPR;
+                if (b0 + i * RPP < rows) {
+                    int q[8];
+                    uint32_t sbits;
+                    quant_piece<7, LPR>(raw[i], q, sbits);
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w |= (uint32_t)(q[e] & 0xF) << (4 * e);
+                    if (r < rows) {
+                        const int64_t row = rowbase + r;
+                        st_nt(w, out + sg.oc[2] + row * (D / 2) + part * 4);
+                        if (part == 0)
+                            *reinterpret_cast<uint16_t*>(out + sg.os[2] + row * 2) =
+                                (uint16_t)sbits;
+                    }
+                }
+            }
         }
-        if (part == 0)
-            *reinterpret_cast<uint16_t*>(out + sg.os[t] + row * 2) = (uint16_t)sbits;
     }
 }
 
@@ -161,33 +230,7 @@ __device__ __forceinline__ int sext4(uint32_t w, int nib) {
     return ((int)(w << (28 - 4 * nib))) >> 28;
 }
 
-// Dequantize the row part of lane `part` for tier t into 8 fp16 values.
-template <int D>
-__device__ __forceinline__ uint4 load_row_part(const uint8_t* __restrict__ in,
-                                               const Segs& sg, uint32_t t, int64_t row,
-                                               int part) {
-    if (t == 0u)
-        return *reinterpret_cast<const uint4*>(in + sg.oc[0] + row * (2 * D) + part * 16);
-    const float s = h2f(*reinterpret_cast<const uint16_t*>(in + sg.os[t] + row * 2));
-    uint4 o;
-    if (t == 1u) {
-        const uint2 w = *reinterpret_cast<const uint2*>(in + sg.oc[1] + row * D + part * 8);
-        o.x = deq_pair(sext8(w.x, 0), sext8(w.x, 1), s);
-        o.y = deq_pair(sext8(w.x, 2), sext8(w.x, 3), s);
-        o.z = deq_pair(sext8(w.y, 0), sext8(w.y, 1), s);
-        o.w = deq_pair(sext8(w.y, 2), sext8(w.y, 3), s);
-    } else {
-        const uint32_t w =
-            *reinterpret_cast<const uint32_t*>(in + sg.oc[2] + row * (D / 2) + part * 4);
-        o.x = deq_pair(sext4(w, 0), sext4(w, 1), s);
-        o.y = deq_pair(sext4(w, 2), sext4(w, 3), s);
-        o.z = deq_pair(sext4(w, 4), sext4(w, 5), s);
-        o.w = deq_pair(sext4(w, 6), sext4(w, 7), s);
-    }
-    return o;
-}
-
-template <int D, bool PAGED>
+template <int D, int NB, bool PAGED>
 __global__ __launch_bounds__(kWaves * 64) void unpack_kernel(
     const uint8_t* __restrict__ in, const uint32_t* __restrict__ map, Segs sg, int64_t n,
     int H, uint16_t* __restrict__ Ko, uint16_t* __restrict__ Vo,
@@ -195,7 +238,7 @@ __global__ __launch_bounds__(kWaves * 64) void unpack_kernel(
     constexpr int LPR = D / 8;
     constexpr int RPP = 64 / LPR;
     const int lane = threadIdx.x & 63;
-    const int64_t j = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t j = wave_token();
     const int64_t layer = blockIdx.y;
     if (j >= n) return;
     const uint32_t m = map[j];
@@ -213,23 +256,86 @@ __global__ __launch_bounds__(kWaves * 64) void unpack_kernel(
     const int part = lane % LPR;
     const int rows = 2 * H;
     const int64_t rowbase = (layer * sg.cnt[t] + slot) * rows;
-    for (int r0 = 0; r0 < rows; r0 += RPP) {
-        const int r = r0 + lane / LPR;
-        if (r >= rows) break;
-        const uint4 o = load_row_part<D>(in, sg, t, rowbase + r, part);
-        uint16_t* dst = (r < H ? Ko : Vo) + (dstrow + (r < H ? r : r - H)) * D + part * 8;
-        *reinterpret_cast<uint4*>(dst) = o;
+    for (int b0 = 0; b0 < rows; b0 += NB * RPP) {
+        // codes (and scales) of the whole batch first, then dequantize; the
+        // tier is uniform across the wavefront
+        uint4 c[NB];
+        float sc[NB];
+        if (t == 0u) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int64_t row = rowbase + min(b0 + i * RPP + lane / LPR, rows - 1);
+                c[i] = *reinterpret_cast<const uint4*>(in + sg.oc[0] + row * (2 * D) + part * 16);
+            }
+        } else if (t == 1u) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int64_t row = rowbase + min(b0 + i * RPP + lane / LPR, rows - 1);
+                const uint2 w = *reinterpret_cast<const uint2*>(in + sg.oc[1] + row * D + part * 8);
+                c[i] = make_uint4(w.x, w.y, 0u, 0u);
+                sc[i] = h2f(*reinterpret_cast<const uint16_t*>(in + sg.os[1] + row * 2));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int64_t row = rowbase + min(b0 + i * RPP + lane / LPR, rows - 1);
+                c[i] = make_uint4(
+                    *reinterpret_cast<const uint32_t*>(in + sg.oc[2] + row * (D / 2) + part * 4),
+                    0u, 0u, 0u);
+                sc[i] = h2f(*reinterpret_cast<const uint16_t*>(in + sg.os[2] + row * 2));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int r = b0 + i * RPP + lane / LPR;
+            uint4 o;
+            if (t == 0u) {
+                o = c[i];
+            } else if (t == 1u) {
+                const float s = sc[i];
+                o.x = deq_pair(sext8(c[i].x, 0), sext8(c[i].x, 1), s);
+                o.y = deq_pair(sext8(c[i].x, 2), sext8(c[i].x, 3), s);
+                o.z = deq_pair(sext8(c[i].y, 0), sext8(c[i].y, 1), s);
+                o.w = deq_pair(sext8(c[i].y, 2), sext8(c[i].y, 3), s);
+            } else {
+                const float s = sc[i];
+                const uint32_t w = c[i].x;
+                o.x = deq_pair(sext4(w, 0), sext4(w, 1), s);
+                o.y = deq_pair(sext4(w, 2), sext4(w, 3), s);
+                o.z = deq_pair(sext4(w, 4), sext4(w, 5), s);
+                o.w = deq_pair(sext4(w, 6), sext4(w, 7), s);
+            }
+            if (r < rows)
+                st_nt(o, (r < H ? Ko : Vo) + (dstrow + (r < H ? r : r - H)) * D + part * 8);
+        }
     }
 }
 
+// Loads batched per wavefront: the power of two (up to kMaxBatch) that
+// covers the 2H rows of a token, in steps of 64 / (D/8) rows.
+int batch_steps(int d, int H) {
+    const int steps = (2 * H + 64 / (d / 8) - 1) / (64 / (d / 8));
+    int nb = 1;
+    while (nb < steps && nb < kMaxBatch) nb *= 2;
+    return nb;
+}
+
 template <typename F>
-hipError_t dispatch_d(int d, F&& f) {
+hipError_t dispatch_d(int d, int H, F&& f) {
+#define SK_NB_CASES(DV)                                                                   \
+    switch (batch_steps(DV, H)) {                                                         \
+        case 1: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 1>{}); \
+        case 2: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 2>{}); \
+        case 4: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 4>{}); \
+        default: return f(std::integral_constant<int, DV>{}, std::integral_constant<int, 8>{}); \
+    }
     switch (d) {
-        case 64: return f(std::integral_constant<int, 64>{});
-        case 128: return f(std::integral_constant<int, 128>{});
-        case 256: return f(std::integral_constant<int, 256>{});
+        case 64: SK_NB_CASES(64)
+        case 128: SK_NB_CASES(128)
+        case 256: SK_NB_CASES(256)
         default: return hipErrorInvalidValue;
     }
+#undef SK_NB_CASES
 }
 
 }  // namespace
@@ -238,8 +344,9 @@ hipError_t launch_pack(const Dims& s, const TierSeg seg[3], const void* k, const
                        const uint32_t* map, void* payload, hipStream_t st) {
     const Segs sg = make_segs(seg);
     const dim3 grid((unsigned)((s.n + kWaves - 1) / kWaves), (unsigned)s.L);
-    return dispatch_d(s.d, [&](auto D) {
-        hipLaunchKernelGGL((pack_kernel<decltype(D)::value>), grid, dim3(kWaves * 64), 0, st,
+    return dispatch_d(s.d, s.Hkv, [&](auto D, auto NB) {
+        hipLaunchKernelGGL((pack_kernel<decltype(D)::value, decltype(NB)::value>), grid,
+                           dim3(kWaves * 64), 0, st,
                            (const uint16_t*)k, (const uint16_t*)v, map, (uint8_t*)payload, sg,
                            s.n, s.Hkv);
         return hipGetLastError();
@@ -251,9 +358,9 @@ hipError_t launch_unpack_dense(const Dims& s, const TierSeg seg[3], const void* 
                                hipStream_t st) {
     const Segs sg = make_segs(seg);
     const dim3 grid((unsigned)((s.n + kWaves - 1) / kWaves), (unsigned)s.L);
-    return dispatch_d(s.d, [&](auto D) {
-        hipLaunchKernelGGL((unpack_kernel<decltype(D)::value, false>), grid, dim3(kWaves * 64),
-                           0, st, (const uint8_t*)payload, map, sg, s.n, s.Hkv,
+    return dispatch_d(s.d, s.Hkv, [&](auto D, auto NB) {
+        hipLaunchKernelGGL((unpack_kernel<decltype(D)::value, decltype(NB)::value, false>), grid,
+                           dim3(kWaves * 64), 0, st, (const uint8_t*)payload, map, sg, s.n, s.Hkv,
                            (uint16_t*)k_out, (uint16_t*)v_out, (const int32_t*)nullptr, 1,
                            (int64_t)0);
         return hipGetLastError();
@@ -266,9 +373,9 @@ hipError_t launch_unpack_paged(const Dims& s, const TierSeg seg[3], const void* 
                                int64_t num_blocks, hipStream_t st) {
     const Segs sg = make_segs(seg);
     const dim3 grid((unsigned)((s.n + kWaves - 1) / kWaves), (unsigned)s.L);
-    return dispatch_d(s.d, [&](auto D) {
-        hipLaunchKernelGGL((unpack_kernel<decltype(D)::value, true>), grid, dim3(kWaves * 64),
-                           0, st, (const uint8_t*)payload, map, sg, s.n, s.Hkv,
+    return dispatch_d(s.d, s.Hkv, [&](auto D, auto NB) {
+        hipLaunchKernelGGL((unpack_kernel<decltype(D)::value, decltype(NB)::value, true>), grid,
+                           dim3(kWaves * 64), 0, st, (const uint8_t*)payload, map, sg, s.n, s.Hkv,
                            (uint16_t*)k_cache, (uint16_t*)v_cache, block_table, block_size,
                            num_blocks);
         return hipGetLastError();
