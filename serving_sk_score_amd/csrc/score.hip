@@ -164,14 +164,14 @@ __device__ __forceinline__ float tile_expsum(const floatx16& a, float c2, float 
 
 // Exact online-softmax update of one lane's (m, s) with the 16 elements of a
 // pass-1 C tile (rows = keys kt0 + crow, column = query qi).  With `masked`,
-// keys above the query are excluded.
-__device__ __forceinline__ void exact_update(const floatx16& a, float c2, bool masked,
-                                             int64_t kt0, int64_t qi, int lane, float& m,
-                                             float& s) {
+// keys above the query are excluded: `lim` = qi - kt0, and row crow is kept
+// while crow <= lim.
+__device__ __forceinline__ void exact_update(const floatx16& a, float c2, bool masked, int lim,
+                                             int lane, float& m, float& s) {
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const bool keep = !masked || kt0 + crow(e, lane) <= qi;
+        const bool keep = !masked || crow(e, lane) <= lim;
         mx = fmaxf(mx, keep ? a[e] * c2 : -INFINITY);
     }
     const float mn = fmaxf(m, mx);
@@ -179,7 +179,7 @@ __device__ __forceinline__ void exact_update(const floatx16& a, float c2, bool m
     float acc = (m == -INFINITY) ? 0.0f : s * ex2(m - mn);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const bool keep = !masked || kt0 + crow(e, lane) <= qi;
+        const bool keep = !masked || crow(e, lane) <= lim;
         acc += keep ? ex2(fmaf(a[e], c2, -mn)) : 0.0f;
     }
     s = acc;
@@ -201,8 +201,8 @@ __device__ __forceinline__ void fixed_ref_update(const floatx16 (&a)[2], float c
         s[0] += t0;
         s[1] += t1;
     } else {
-        exact_update(a[0], c2, false, 0, 0, lane, m[0], s[0]);
-        exact_update(a[1], c2, false, 0, 0, lane, m[1], s[1]);
+        exact_update(a[0], c2, false, 0, lane, m[0], s[0]);
+        exact_update(a[1], c2, false, 0, lane, m[1], s[1]);
     }
 }
 
@@ -287,8 +287,9 @@ __global__ __launch_bounds__(W * QW * 64, D == 256 ? 1 : 2) void rowlse_kernel(
                 if (need0) acc0 = mfma32(a, qf[0][c], acc0);
                 acc1 = mfma32(a, qf[1][c], acc1);
             }
-            if (need0) exact_update(acc0, c2, kt0 + 31 > q0, kt0, q0 + col, lane, m[0], s[0]);
-            exact_update(acc1, c2, kt0 + 31 > q0 + 32, kt0, q0 + 32 + col, lane, m[1], s[1]);
+            const int lim = (int)(q0 - kt0) + col;  // query - first key of the tile
+            if (need0) exact_update(acc0, c2, kt0 + 31 > q0, lim, lane, m[0], s[0]);
+            exact_update(acc1, c2, kt0 + 31 > q0 + 32, lim + 32, lane, m[1], s[1]);
         }
         next_stage(si);
     }
@@ -369,15 +370,15 @@ __device__ __forceinline__ float tile_colsum(const floatx16& a, const float (&L)
     return (s0 + s1) + (s2 + s3);
 }
 
-// Same on a diagonal tile: only rows (queries) at or after the lane's key.
+// Same on a diagonal tile: only rows (queries) at or after the lane's key,
+// i.e. rows crow >= first = key - (first query of the tile).
 __device__ __forceinline__ float tile_colsum_masked(const floatx16& a, const float (&L)[16],
-                                                    float c2, int64_t it0, int64_t key,
-                                                    int lane) {
+                                                    float c2, int first, int lane) {
     float s = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const float p = ex2(fmaf(a[e], c2, -L[e]));
-        s += (it0 + crow(e, lane) >= key) ? p : 0.0f;
+        s += (crow(e, lane) >= first) ? p : 0.0f;
     }
     return s;
 }
@@ -499,8 +500,9 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
                     acc0 = mfma32(a, kf[0][c], acc0);
                     if (need1) acc1 = mfma32(a, kf[1][c], acc1);
                 }
-                cs[0] += tile_colsum_masked(acc0, L, c2, it0, k0 + col, lane);
-                if (need1) cs[1] += tile_colsum_masked(acc1, L, c2, it0, k0 + 32 + col, lane);
+                const int first = (int)(k0 - it0) + col;  // key - first query of the tile
+                cs[0] += tile_colsum_masked(acc0, L, c2, first, lane);
+                if (need1) cs[1] += tile_colsum_masked(acc1, L, c2, first + 32, lane);
             }
         }
         if (si + 1 < ns) {
