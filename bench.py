@@ -184,8 +184,8 @@ def main():
 
     dom = "colsum" if mean_launch["colsum"] >= mean_launch["rowlse"] else "rowlse"
     ach = pass_flops / (mean_launch[dom] * 1e-3) / 1e12
-    W = 4 if Hq // Hkv == 4 else Hq // Hkv   # heads per workgroup of the launch timed
-    kernel_name = f"{dom}_kernel<{d},{W}>"
+    kernel_name = score_kernel_names(Hq, Hkv, d)[dom]
+    nb = pack_batch(Hkv, d)
 
     def rl(bytes_, sec, kernel):
         gbs = bytes_ / sec / 1e9
@@ -222,9 +222,10 @@ def main():
                      "traffic": counted_traffic(kernel_name),
                      "flops_per_launch": pass_flops,
                      "avg_launch_ms": round(mean_launch[dom], 4)},
-        "roofline_stages": {"pack": rl(pack_bytes, t_pack, f"pack_kernel<{d}>"),
-                            "unpack": rl(unpack_bytes, t_unpack, f"unpack_kernel<{d},dense>"),
-                            "unpack_paged": rl(unpack_bytes, t_paged, f"unpack_kernel<{d},paged>")},
+        "roofline_stages": {"pack": rl(pack_bytes, t_pack, f"pack_kernel<{d},{nb}>"),
+                            "unpack": rl(unpack_bytes, t_unpack, f"unpack_kernel<{d},{nb},false>"),
+                            "unpack_paged": rl(unpack_bytes, t_paged,
+                                               f"unpack_kernel<{d},{nb},true>")},
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "copy_bytes": int(src.numel()),
         "wall_s_timed": round(wall, 3),
@@ -232,6 +233,30 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def score_kernel_names(Hq, Hkv, d):
+    """Template instances the library launches for this shape (the rule of
+    its launchers: W = largest divisor of Hq/Hkv up to 8 heads per row-pass
+    workgroup, QW = 4/W blocks of 64 queries when W < 3, stages of 64 rows,
+    32 at d = 256; the column pass uses 4 wavefronts)."""
+    R = Hq // Hkv
+    W = max(w for w in range(1, 9) if R % w == 0)
+    QW = 1 if W >= 3 else 4 // W
+    KS = 32 if d == 256 else 64
+    return {"rowlse": f"rowlse_kernel<{d},{W},{QW},{KS}>",
+            "colsum": f"colsum_kernel<{d},4,{KS}>"}
+
+
+def pack_batch(Hkv, d):
+    """Rows steps whose loads the pack/unpack kernels batch per token (the
+    power of two, up to 8, covering 2*Hkv rows at 64/(d/8) rows a step)."""
+    rpp = 64 // (d // 8)
+    steps = (2 * Hkv + rpp - 1) // rpp
+    nb = 1
+    while nb < steps and nb < 8:
+        nb *= 2
+    return nb
 
 
 def counted_traffic(kernel):

@@ -529,12 +529,22 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
     }
 }
 
+// score[j] (+)= sum over the P per-head partial rows, added in head order.
+// The loads of 8 heads are issued together; the additions stay sequential.
 __global__ void reduce_kernel(const float* __restrict__ partial, int64_t ldp, int P,
                               int64_t n, float* __restrict__ score, int acc) {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n) return;
     float v = 0.0f;
-    for (int p = 0; p < P; ++p) v += partial[(int64_t)p * ldp + j];
+    int p = 0;
+    for (; p + 8 <= P; p += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = partial[(int64_t)(p + u) * ldp + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += x[u];
+    }
+    for (; p < P; ++p) v += partial[(int64_t)p * ldp + j];
     score[j] = acc ? score[j] + v : v;
 }
 
