@@ -150,10 +150,16 @@ struct Stager {
 };
 
 // Sum over the 16 elements of a C tile of 2^(c2 x - m), in four chains.
+// (Each chain starts from its first term rather than 0.0f + term: the terms
+// are >= 0, so the sums are the same, without an add the compiler may not
+// drop under IEEE signed-zero rules.)
 __device__ __forceinline__ float tile_expsum(const floatx16& a, float c2, float m) {
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    float s0 = ex2(fmaf(a[0], c2, -m));
+    float s1 = ex2(fmaf(a[1], c2, -m));
+    float s2 = ex2(fmaf(a[2], c2, -m));
+    float s3 = ex2(fmaf(a[3], c2, -m));
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) {
+    for (int e = 4; e < 16; e += 4) {
         s0 += ex2(fmaf(a[e + 0], c2, -m));
         s1 += ex2(fmaf(a[e + 1], c2, -m));
         s2 += ex2(fmaf(a[e + 2], c2, -m));
@@ -359,9 +365,12 @@ __device__ __forceinline__ void load_rows(const float* v32, int lane, float (&L)
 
 // Sum over the 16 elements of a pass-2 C tile of 2^(c2 x - L[e]).
 __device__ __forceinline__ float tile_colsum(const floatx16& a, const float (&L)[16], float c2) {
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    float s0 = ex2(fmaf(a[0], c2, -L[0]));
+    float s1 = ex2(fmaf(a[1], c2, -L[1]));
+    float s2 = ex2(fmaf(a[2], c2, -L[2]));
+    float s3 = ex2(fmaf(a[3], c2, -L[3]));
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) {
+    for (int e = 4; e < 16; e += 4) {
         s0 += ex2(fmaf(a[e + 0], c2, -L[e + 0]));
         s1 += ex2(fmaf(a[e + 1], c2, -L[e + 1]));
         s2 += ex2(fmaf(a[e + 2], c2, -L[e + 2]));
