@@ -13,7 +13,9 @@ and k_j is the key of KV head g = h // (H_q / H_kv) (contiguous GQA groups).
 Readings:
 
 * lambda = 0, so I_j = A_j: the recency factor exp(-lambda Delta_j) of §4.3 is
-  printed without definitions of Delta_j or lambda.
+  printed without definitions of Delta_j or lambda.  The lambda > 0 variant
+  and the KV-norm fallback of Algorithm 1 are the two functions at the end
+  of this module, each with its own reading.
 * A sum over heads and layers, not a mean (a positive factor does not change
   the ranking).
 * The diagonal i = j is included (a causal softmax includes the token itself).
@@ -129,3 +131,38 @@ def layer_column_sample(q, k, cols, heads=None):
 def to_fp32(score64):
     """The score handed to tier assignment: fp64 rounded to nearest fp32."""
     return np.asarray(score64, dtype=np.float64).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Score variants of Algorithm 1 "score tokens"
+
+def recency_weight(a, lam):
+    """I_j = A_j * exp(-lambda * Delta_j)   (SpectrumKV §4.3, the printed
+    importance formula).
+
+    Reading: the page does not define Delta_j; it is taken as the distance
+    of token j from the last prefill token, Delta_j = n - 1 - j, so that
+    lambda > 0 favours recent tokens and lambda = 0 gives I_j = A_j.
+    float64 throughout."""
+    a = np.asarray(a, dtype=np.float64)
+    n = a.shape[0]
+    delta = (n - 1) - np.arange(n, dtype=np.float64)
+    return a * np.exp(-float(lam) * delta)
+
+
+def kv_norm_score(ks):
+    """KV-norm fallback of Algorithm 1 ("compute I_j ... or a KV-norm
+    fallback").
+
+    Reading: the page names the fallback without a formula; it is taken as
+    the sum over layers and KV heads of the Euclidean norm of the token's
+    key vector, score_j = sum_l sum_g ||k[l][j][g]||_2.
+    ks: [L][n][H_kv][d] (fp16 widened exactly to float64)."""
+    ks = np.asarray(ks, dtype=np.float64)
+    L, n, H, d = ks.shape
+    out = np.zeros(n, dtype=np.float64)
+    for layer in range(L):
+        for g in range(H):
+            out += np.sqrt((ks[layer, :, g, :] ** 2).sum(axis=1))
+    return out
+

@@ -167,3 +167,60 @@ def test_fp32_rounding_is_nearest():
     assert f[0] == np.float32(1.0)                      # tie -> even
     assert f[1] == np.float32(1.0 + 2.0 ** -22)         # tie -> even (up)
     assert abs(float(f[2]) - 0.1) <= 2.0 ** -28
+
+
+# ---------------------------------------------------------------- variants --
+# Recency weighting I_j = A_j exp(-lambda Delta_j) and the KV-norm fallback
+# (Algorithm 1 "score tokens").  Pins: closed forms, brute force with scalar
+# math on tiny inputs, exact scaling.
+
+def test_recency_lambda_zero_is_identity():
+    a = np.random.default_rng(1).random(37) * 10
+    assert np.array_equal(SC.recency_weight(a, 0.0), a)
+
+
+def test_recency_closed_form_on_constant_scores():
+    n, lam = 50, 0.07
+    w = SC.recency_weight(np.full(n, 3.0), lam)
+    assert w[-1] == 3.0                                   # Delta = 0 for the last token
+    assert w[0] == pytest.approx(3.0 * math.exp(-lam * (n - 1)), rel=1e-15)
+    ratio = w[1:] / w[:-1]
+    assert np.allclose(ratio, math.exp(lam), rtol=1e-14)  # geometric in the position
+    assert np.all(np.diff(w) > 0)                         # recent tokens rank higher
+
+
+def test_recency_brute_force():
+    rng = np.random.default_rng(2)
+    for n in (1, 2, 9):
+        a = rng.random(n) * 5
+        lam = float(rng.random())
+        want = [a[j] * math.exp(-lam * (n - 1 - j)) for j in range(n)]
+        assert np.allclose(SC.recency_weight(a, lam), want, rtol=1e-15, atol=0)
+
+
+def test_kv_norm_constant_keys():
+    L, n, H, d = 3, 5, 2, 64
+    ks = np.full((L, n, H, d), -0.75, dtype=np.float16)
+    want = L * H * 0.75 * math.sqrt(d)
+    assert np.allclose(SC.kv_norm_score(ks), want, rtol=1e-14)
+
+
+def test_kv_norm_brute_force_and_scaling():
+    rng = np.random.default_rng(3)
+    L, n, H, d = 2, 4, 3, 8
+    ks = rng.standard_normal((L, n, H, d)).astype(np.float16)
+    want = []
+    for j in range(n):
+        tot = 0.0
+        for layer in range(L):
+            for g in range(H):
+                tot += math.sqrt(sum(float(x) ** 2 for x in ks[layer, j, g]))
+        want.append(tot)
+    got = SC.kv_norm_score(ks)
+    assert np.allclose(got, want, rtol=1e-13)
+    # doubling every key (exact in fp16 here) doubles every score exactly
+    assert np.array_equal(SC.kv_norm_score(ks * np.float16(2)), 2 * got)
+    # a key with a single non-zero element contributes its magnitude
+    one = np.zeros((1, 1, 1, d), dtype=np.float16)
+    one[0, 0, 0, 3] = -5.5
+    assert SC.kv_norm_score(one)[0] == 5.5
