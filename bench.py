@@ -165,6 +165,24 @@ def main():
     wall = time.time() - wall0
     ms_per_step = start.elapsed_time(end) / args.steps
 
+    # the score variants of the same request, timed on their own (they replace
+    # or reweight the score; they are not part of the step)
+    def timed(fn, reps):
+        fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    alt = torch.empty(n, dtype=torch.float32, device=dev)
+    reps = max(3, args.steps)
+    t_kvnorm = timed(lambda: sk.score_kvnorm(shape, K, alt), reps) * 1e-3
+    t_recency = timed(lambda: sk.recency_weight(score, 1e-3, alt), reps) * 1e-3
+
     # per stage: [steps][launches] durations in ms
     t = {s: np.array([[e[s][2 * j].elapsed_time(e[s][2 * j + 1]) for j in range(len(e[s]) // 2)]
                       for e in all_ev]) for s in stages}
@@ -226,6 +244,10 @@ def main():
                             "unpack": rl(unpack_bytes, t_unpack, f"unpack_kernel<{d},{nb},false>"),
                             "unpack_paged": rl(unpack_bytes, t_paged,
                                                f"unpack_kernel<{d},{nb},true>")},
+        "variants": {"kvnorm": rl(kv_bytes // 2 + 4 * n, t_kvnorm, f"kvnorm_kernel<{d}>"),
+                     # n = 8192 elements: one launch's latency, not a bandwidth figure
+                     "recency": {"bound": "latency", "kernel": "recency_kernel",
+                                 "us_per_launch": round(t_recency * 1e6, 2)}},
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "copy_bytes": int(src.numel()),
         "wall_s_timed": round(wall, 3),

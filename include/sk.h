@@ -3,7 +3,8 @@
  *
  * The operations follow the SpectrumKV paper (arXiv 2606.08635):
  *   - importance score            : §4.3 (I_j = A_j with lambda = 0) and
- *                                    Algorithm 1 "score tokens"
+ *                                    Algorithm 1 "score tokens"; its recency
+ *                                    weighting and KV-norm fallback
  *   - tier assignment             : §4.4 budget-to-tier mapping, §7.4.1 sink
  *                                    pinning, §2.3 Proposition 1 (sorted
  *                                    assignment), Algorithm 1 "assign tiers"
@@ -154,6 +155,35 @@ sk_status sk_score_colsum(const sk_shape* shape, int64_t n_tokens,
                           const void* q, const void* k, const float* lse,
                           float* score, int32_t accumulate,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------- score variants --
+ * The other two options of Algorithm 1 "score tokens".
+ *
+ * Recency weighting, the §4.3 importance formula I_j = A_j exp(-lambda Delta_j):
+ *   score_out[j] = fp32_rn(score_in[j] * exp(-lambda * (n - 1 - j)))
+ * evaluated in double precision.  The page defines neither Delta_j nor
+ * lambda; Delta_j is read as the distance of token j from the last prefill
+ * token, so lambda > 0 ranks recent tokens higher and lambda = 0 returns the
+ * input unchanged.  Apply it once, after the last layer's sk_score.
+ *   score_in, score_out : fp32 [n]; they may be the same buffer (in place)
+ *   lambda              : finite and >= 0, else SK_E_ARG */
+sk_status sk_recency_weight(int64_t n_tokens, double lambda, const float* score_in,
+                            float* score_out, void* stream);
+
+/* KV-norm fallback (Algorithm 1 "score tokens"): a score that needs no
+ * queries.  The page names it without a formula; it is read as the sum of the
+ * Euclidean norms of the token's keys over layers and KV heads:
+ *   score_j = sum_l sum_g || k[l][j][g][:] ||_2
+ *   k     : fp16 [n_layers][n][n_kv_heads][head_dim] (the layout sk_pack
+ *           reads; a caller holding one buffer per layer passes
+ *           n_layers = 1 and accumulates)
+ *   score : fp32 [n]; overwritten (accumulate = 0) or added to (1)
+ * Sums of squares, square roots and the sum over (l, g) are fp32 in a fixed
+ * order, so the result is deterministic; its relative error is at most
+ * (m + 16) * 2^-24 with m = ceil(n_layers * ceil(n_kv_heads * head_dim / 512) / 8)
+ * (2e-6 for 32 layers x 8 heads x 128). */
+sk_status sk_score_kvnorm(const sk_shape* shape, int64_t n_tokens, const void* k,
+                          float* score, int32_t accumulate, void* stream);
 
 /* --------------------------------------------------------------- assign --
  * Tier assignment (§7.4.1 sinks, §2.3 sorted assignment, §4.4 counts):

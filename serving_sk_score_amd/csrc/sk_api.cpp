@@ -259,6 +259,36 @@ sk_status sk_score(const sk_shape* shape, int64_t n, const void* q, const void* 
     return device(sk::launch_reduce(d, partial, score, accumulate, st), "reduce");
 }
 
+sk_status sk_recency_weight(int64_t n, double lambda, const float* in, float* out,
+                            void* stream) {
+    if (sk_status st = check_tokens(n)) return st;
+    if (!std::isfinite(lambda) || lambda < 0.0)
+        return fail(SK_E_ARG, "lambda must be finite and >= 0");
+    if (n == 0) return ok();
+    if (!in || !out) return fail(SK_E_ARG, "score_in and score_out must be non-NULL");
+    if (!aligned(in, 4) || !aligned(out, 4))
+        return fail(SK_E_ARG, "score_in and score_out must be 4-byte aligned");
+    if (in != out && (const char*)in < (const char*)(out + n) &&
+        (const char*)out < (const char*)(in + n))
+        return fail(SK_E_ARG, "score_in and score_out overlap without being the same buffer");
+    (void)hipGetLastError();
+    return device(sk::launch_recency(n, lambda, in, out, (hipStream_t)stream), "recency");
+}
+
+sk_status sk_score_kvnorm(const sk_shape* shape, int64_t n, const void* k, float* score,
+                          int32_t accumulate, void* stream) {
+    if (sk_status st = check_shape(shape)) return st;
+    if (sk_status st = check_tokens(n)) return st;
+    if (accumulate != 0 && accumulate != 1) return fail(SK_E_ARG, "accumulate must be 0 or 1");
+    if (n == 0) return ok();
+    if (!k || !score) return fail(SK_E_ARG, "k and score must be non-NULL");
+    if (!aligned(k, 16)) return fail(SK_E_ARG, "k must be 16-byte aligned");
+    if (!aligned(score, 4)) return fail(SK_E_ARG, "score must be 4-byte aligned");
+    (void)hipGetLastError();
+    return device(sk::launch_kvnorm(dims(shape, n), k, score, accumulate, (hipStream_t)stream),
+                  "kvnorm");
+}
+
 size_t sk_assign_workspace_bytes(int64_t n) {
     (void)n;
     return 0;

@@ -49,4 +49,10 @@ hipError_t launch_unpack_paged(const Dims& s, const TierSeg seg[3], const void* 
                                const int32_t* block_table, int32_t block_size,
                                int64_t num_blocks, hipStream_t st);
 
+// score variants: KV-norm fallback (score fp32 [n]) and recency weighting
+hipError_t launch_kvnorm(const Dims& s, const void* k, float* score, int accumulate,
+                         hipStream_t st);
+hipError_t launch_recency(int64_t n, double lambda, const float* in, float* out,
+                          hipStream_t st);
+
 }  // namespace sk

@@ -23,7 +23,7 @@ EXPORTS = [
     "sk_plan_make", "sk_score_workspace_bytes", "sk_score", "sk_score_rowlse",
     "sk_score_colsum_workspace_bytes", "sk_score_colsum", "sk_assign_workspace_bytes",
     "sk_assign_tiers", "sk_pack", "sk_unpack", "sk_status_string", "sk_last_error",
-    "sk_layout_version",
+    "sk_layout_version", "sk_recency_weight", "sk_score_kvnorm",
 ]
 
 
@@ -110,6 +110,8 @@ def lib():
             "sk_status_string": (ctypes.c_char_p, [i32]),
             "sk_last_error": (ctypes.c_char_p, []),
             "sk_layout_version": (i32, []),
+            "sk_recency_weight": (i32, [i64, ctypes.c_double, vp, vp, vp]),
+            "sk_score_kvnorm": (i32, [P(_Shape), i64, vp, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -218,6 +220,27 @@ def score_colsum(shape: Shape, q, k, lse, out, accumulate=False, ws=None):
     _check(lib().sk_score_colsum(ctypes.byref(shape.c()), n, _ptr(q), _ptr(k), _ptr(lse),
                                  _ptr(out), int(bool(accumulate)), _ptr(ws), ws.numel(),
                                  _stream(q)))
+    return out
+
+
+def recency_weight(score_in, lam, out=None):
+    """out[j] = score_in[j] * exp(-lam * (n - 1 - j)); out may be score_in."""
+    n = score_in.shape[0] if score_in.dim() == 1 else -1
+    _need(score_in, "score_in", torch.float32, shape=(n,))
+    if out is None:
+        out = torch.empty_like(score_in)
+    _need(out, "score_out", torch.float32, shape=(n,))
+    _check(lib().sk_recency_weight(n, float(lam), _ptr(score_in), _ptr(out), _stream(score_in)))
+    return out
+
+
+def score_kvnorm(shape: Shape, k, out, accumulate=False):
+    """KV-norm fallback score of k (fp16 [L][n][H_kv][d]) into out (fp32 [n])."""
+    n = k.shape[1] if k.dim() == 4 else -1
+    _need(k, "k", torch.float16, shape=_kv_shape(shape, n))
+    _need(out, "score", torch.float32, shape=(n,))
+    _check(lib().sk_score_kvnorm(ctypes.byref(shape.c()), n, _ptr(k), _ptr(out),
+                                 int(bool(accumulate)), _stream(k)))
     return out
 
 

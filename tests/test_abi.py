@@ -142,6 +142,18 @@ def test_call_validation_without_device():
     pg0 = sk._Paged(0x7F0000001000, 0x7F0000001000, 0x7F0000001000, 0, 7)
     assert lib.sk_unpack(B(shape), B(pc), FAKE, FAKE, None, None, B(pg0), None) == sk.SK_E_ARG
     assert lib.sk_unpack(B(shape), B(pc), FAKE, FAKE, FAKE, FAKE, B(pg), None) == sk.SK_E_ARG
+    # score variants: lambda out of range, overlap, NULLs, accumulate flag
+    assert lib.sk_recency_weight(10, -0.5, FAKE, FAKE, None) == sk.SK_E_ARG
+    assert lib.sk_recency_weight(10, float("nan"), FAKE, FAKE, None) == sk.SK_E_ARG
+    assert lib.sk_recency_weight(10, 0.5, None, FAKE, None) == sk.SK_E_ARG
+    assert lib.sk_recency_weight(10, 0.5, FAKE, ctypes.c_void_p(0x7F0000001008), None) == sk.SK_E_ARG
+    assert lib.sk_recency_weight(-1, 0.5, FAKE, FAKE, None) == sk.SK_E_ARG
+    assert lib.sk_recency_weight(0, 0.5, None, None, None) == sk.SK_OK
+    assert lib.sk_score_kvnorm(B(shape), 10, None, FAKE, 0, None) == sk.SK_E_ARG
+    assert lib.sk_score_kvnorm(B(shape), 10, FAKE_MIS, FAKE, 0, None) == sk.SK_E_ARG
+    assert lib.sk_score_kvnorm(B(shape), 10, FAKE, FAKE, 2, None) == sk.SK_E_ARG
+    assert lib.sk_score_kvnorm(B(bad_shape), 10, FAKE, FAKE, 0, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_score_kvnorm(B(shape), 0, None, None, 0, None) == sk.SK_OK
     empty = _plan((2, 4, 2, 64), (0, 4, 1, 0.5))
     assert lib.sk_pack(B(shape), B(empty.c), None, None, None, None, None, None) == sk.SK_OK
     assert lib.sk_unpack(B(shape), B(empty.c), None, None, None, None, None, None) == sk.SK_OK
