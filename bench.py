@@ -183,6 +183,16 @@ def main():
     t_kvnorm = timed(lambda: sk.score_kvnorm(shape, K, alt), reps) * 1e-3
     t_recency = timed(lambda: sk.recency_weight(score, 1e-3, alt), reps) * 1e-3
 
+    # cold-tier upgrade of n/8 seeded tokens: fp16 gather, then the paged scatter
+    n_up = n // 8
+    up_tokens = torch.from_numpy(
+        np.random.default_rng(1).choice(n, size=n_up, replace=False).astype(np.int32)).to(dev)
+    up_payload = torch.empty(sk.upgrade_bytes(shape, n_up), dtype=torch.uint8, device=dev)
+    t_up_pack = timed(lambda: sk.upgrade_pack(shape, K, V, up_tokens, up_payload), reps) * 1e-3
+    t_up_paged = timed(lambda: sk.upgrade_unpack_paged(shape, n, up_payload, up_tokens, Kc, Vc,
+                                                       block_table, bs), reps) * 1e-3
+    up_bytes = 2 * up_payload.numel() + 4 * n_up                 # rows read + written, list
+
     # per stage: [steps][launches] durations in ms
     t = {s: np.array([[e[s][2 * j].elapsed_time(e[s][2 * j + 1]) for j in range(len(e[s]) // 2)]
                       for e in all_ev]) for s in stages}
@@ -248,6 +258,10 @@ def main():
                      # n = 8192 elements: one launch's latency, not a bandwidth figure
                      "recency": {"bound": "latency", "kernel": "recency_kernel",
                                  "us_per_launch": round(t_recency * 1e6, 2)}},
+        "upgrade": {"tokens": n_up,
+                    "pack": rl(up_bytes, t_up_pack, f"upgrade_pack_kernel<{d},{nb}>"),
+                    "unpack_paged": rl(up_bytes, t_up_paged,
+                                       f"upgrade_unpack_kernel<{d},{nb},true>")},
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "copy_bytes": int(src.numel()),
         "wall_s_timed": round(wall, 3),

@@ -12,6 +12,7 @@
  *                                    independently, one mixed payload), §2.1
  *                                    tier costs
  *   - dequantize (dense or paged) : §4.2 (decode-side dequantization only)
+ *   - cold-tier upgrade           : §4.2 and §8 (cold-tier fetch design)
  *
  * Conventions shared by every entry point
  *   - Ownership: the caller allocates and frees every buffer.  The library
@@ -242,6 +243,33 @@ typedef struct {
 sk_status sk_unpack(const sk_shape* shape, const sk_plan* plan,
                     const void* payload, const uint32_t* map,
                     void* k_out, void* v_out, const sk_paged* paged, void* stream);
+
+/* -------------------------------------------------------------- upgrade --
+ * Cold-tier upgrade (§4.2, and the cold-tier fetch design paragraph of §8):
+ * tokens that reached the decode side at int8 or int4 are raised to fp16
+ * later by re-sending their fp16 rows, which then overwrite the
+ * approximations in the decode-side KV.  The pages give the saving only as a
+ * byte difference; no code shorter than 16 bits per element restores every
+ * fp16 value from its int4 bucket, so the rows are sent whole.
+ *   tokens  : device u32 [n_up], token indices chosen by the caller; an entry
+ *             >= n_tokens is skipped (its payload rows are not written and
+ *             nothing is written for it on unpack); repeats are allowed
+ *   payload : sk_upgrade_bytes(shape, n_up) bytes, 16-byte aligned; row
+ *             r = ((l * n_up + i) * 2 + kv) * n_kv_heads + g holds the fp16
+ *             row of token tokens[i] (the c16 layout of sk_plan with
+ *             N16 = n_up and slot = i), 2 * head_dim bytes each.
+ * sk_upgrade_pack reads k, v as sk_pack does.  sk_upgrade_unpack writes the
+ * rows into dense k_out / v_out (paged == NULL) or into the paged cache
+ * exactly where sk_unpack puts the token (a block id outside the pool is
+ * skipped); all other rows are untouched.
+ * sk_upgrade_bytes returns 0 for an invalid shape or n_up < 0. */
+size_t    sk_upgrade_bytes(const sk_shape* shape, int64_t n_up);
+sk_status sk_upgrade_pack(const sk_shape* shape, int64_t n_tokens, const void* k,
+                          const void* v, const uint32_t* tokens, int64_t n_up,
+                          void* payload, void* stream);
+sk_status sk_upgrade_unpack(const sk_shape* shape, int64_t n_tokens, const void* payload,
+                            const uint32_t* tokens, int64_t n_up, void* k_out, void* v_out,
+                            const sk_paged* paged, void* stream);
 
 /* ------------------------------------------------------------ messages -- */
 const char* sk_status_string(sk_status status);

@@ -311,6 +311,84 @@ __global__ __launch_bounds__(kWaves * 64) void unpack_kernel(
     }
 }
 
+// Cold-tier upgrade: the fp16 rows of a caller-chosen list of tokens,
+// gathered into an upgrade payload (slot i = list entry i, the fp16
+// segment's row order) or scattered from it into the dense KV or the paged
+// cache.  Same mapping as above: one wavefront per (layer, list entry), its
+// 2H rows spread D/8 lanes per row, the loads of NB steps in flight before
+// the stores.  A listed token outside [0, n) is skipped.
+template <int D, int NB>
+__global__ __launch_bounds__(kWaves * 64) void upgrade_pack_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint32_t* __restrict__ tokens, uint8_t* __restrict__ out, int64_t m, int64_t n,
+    int H) {
+    constexpr int LPR = D / 8;
+    constexpr int RPP = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int64_t i = wave_token();
+    const int64_t layer = blockIdx.y;
+    if (i >= m) return;
+    const int64_t j = tokens[i];
+    if (j >= n) return;
+    const int part = lane % LPR;
+    const int rows = 2 * H;
+    const int64_t rowbase = (layer * m + i) * rows;
+    const int64_t tokrow = (layer * n + j) * H;
+    for (int b0 = 0; b0 < rows; b0 += NB * RPP) {
+        uint4 raw[NB];
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+            const int r = min(b0 + s * RPP + lane / LPR, rows - 1);
+            raw[s] = ld_nt((r < H ? K : V) + (tokrow + (r < H ? r : r - H)) * D + part * 8);
+        }
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+            const int r = b0 + s * RPP + lane / LPR;
+            if (r < rows) st_nt(raw[s], out + (rowbase + r) * (2 * D) + part * 16);
+        }
+    }
+}
+
+template <int D, int NB, bool PAGED>
+__global__ __launch_bounds__(kWaves * 64) void upgrade_unpack_kernel(
+    const uint8_t* __restrict__ in, const uint32_t* __restrict__ tokens, int64_t m, int64_t n,
+    int H, uint16_t* __restrict__ Ko, uint16_t* __restrict__ Vo,
+    const int32_t* __restrict__ block_table, int32_t block_size, int64_t num_blocks) {
+    constexpr int LPR = D / 8;
+    constexpr int RPP = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int64_t i = wave_token();
+    const int64_t layer = blockIdx.y;
+    if (i >= m) return;
+    const int64_t j = tokens[i];
+    if (j >= n) return;
+    int64_t dstrow;
+    if (PAGED) {
+        const int64_t blk = block_table[j / block_size];
+        if (blk < 0 || blk >= num_blocks) return;
+        dstrow = ((layer * num_blocks + blk) * block_size + (j % block_size)) * H;
+    } else {
+        dstrow = (layer * n + j) * H;
+    }
+    const int part = lane % LPR;
+    const int rows = 2 * H;
+    const int64_t rowbase = (layer * m + i) * rows;
+    for (int b0 = 0; b0 < rows; b0 += NB * RPP) {
+        uint4 c[NB];
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+            const int64_t row = rowbase + min(b0 + s * RPP + lane / LPR, rows - 1);
+            c[s] = *reinterpret_cast<const uint4*>(in + row * (2 * D) + part * 16);
+        }
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+            const int r = b0 + s * RPP + lane / LPR;
+            if (r < rows)
+                st_nt(c[s], (r < H ? Ko : Vo) + (dstrow + (r < H ? r : r - H)) * D + part * 8);
+        }
+    }
+}
+
 // Loads batched per wavefront: the power of two (up to kMaxBatch) that
 // covers the 2H rows of a token, in steps of 64 / (D/8) rows.
 int batch_steps(int d, int H) {
@@ -378,6 +456,37 @@ hipError_t launch_unpack_paged(const Dims& s, const TierSeg seg[3], const void* 
                            dim3(kWaves * 64), 0, st, (const uint8_t*)payload, map, sg, s.n, s.Hkv,
                            (uint16_t*)k_cache, (uint16_t*)v_cache, block_table, block_size,
                            num_blocks);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_upgrade_pack(const Dims& s, int64_t m, const void* k, const void* v,
+                               const uint32_t* tokens, void* payload, hipStream_t st) {
+    const dim3 grid((unsigned)((m + kWaves - 1) / kWaves), (unsigned)s.L);
+    return dispatch_d(s.d, s.Hkv, [&](auto D, auto NB) {
+        hipLaunchKernelGGL((upgrade_pack_kernel<decltype(D)::value, decltype(NB)::value>), grid,
+                           dim3(kWaves * 64), 0, st, (const uint16_t*)k, (const uint16_t*)v,
+                           tokens, (uint8_t*)payload, m, s.n, s.Hkv);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_upgrade_unpack(const Dims& s, int64_t m, const void* payload,
+                                 const uint32_t* tokens, void* k_out, void* v_out,
+                                 const int32_t* block_table, int32_t block_size,
+                                 int64_t num_blocks, hipStream_t st) {
+    const dim3 grid((unsigned)((m + kWaves - 1) / kWaves), (unsigned)s.L);
+    return dispatch_d(s.d, s.Hkv, [&](auto D, auto NB) {
+        if (block_table)
+            hipLaunchKernelGGL(
+                (upgrade_unpack_kernel<decltype(D)::value, decltype(NB)::value, true>), grid,
+                dim3(kWaves * 64), 0, st, (const uint8_t*)payload, tokens, m, s.n, s.Hkv,
+                (uint16_t*)k_out, (uint16_t*)v_out, block_table, block_size, num_blocks);
+        else
+            hipLaunchKernelGGL(
+                (upgrade_unpack_kernel<decltype(D)::value, decltype(NB)::value, false>), grid,
+                dim3(kWaves * 64), 0, st, (const uint8_t*)payload, tokens, m, s.n, s.Hkv,
+                (uint16_t*)k_out, (uint16_t*)v_out, (const int32_t*)nullptr, 1, (int64_t)0);
         return hipGetLastError();
     });
 }

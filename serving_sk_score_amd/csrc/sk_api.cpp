@@ -372,4 +372,67 @@ sk_status sk_unpack(const sk_shape* shape, const sk_plan* plan, const void* payl
                   "unpack");
 }
 
+size_t sk_upgrade_bytes(const sk_shape* shape, int64_t m) {
+    if (check_shape(shape) || m < 0 || m >= kMaxTokens) return 0;
+    return (size_t)shape->n_layers * (size_t)m * 2 * (size_t)shape->n_kv_heads * 2 *
+           (size_t)shape->head_dim;
+}
+
+static sk_status check_upgrade(const sk_shape* shape, int64_t n, int64_t m,
+                               const uint32_t* tokens, const void* payload) {
+    if (sk_status st = check_shape(shape)) return st;
+    if (sk_status st = check_tokens(n)) return st;
+    if (m < 0 || m >= kMaxTokens) return fail(SK_E_ARG, "n_up %lld outside [0, 2^30)", (long long)m);
+    if (m == 0) return SK_OK;
+    if (!tokens || !payload) return fail(SK_E_ARG, "tokens and payload must be non-NULL");
+    if (!aligned(tokens, 4)) return fail(SK_E_ARG, "tokens must be 4-byte aligned");
+    if (!aligned(payload, 16)) return fail(SK_E_ARG, "payload must be 16-byte aligned");
+    return SK_OK;
+}
+
+sk_status sk_upgrade_pack(const sk_shape* shape, int64_t n, const void* k, const void* v,
+                          const uint32_t* tokens, int64_t m, void* payload, void* stream) {
+    if (sk_status st = check_upgrade(shape, n, m, tokens, payload)) return st;
+    if (m == 0 || n == 0) return ok();
+    if (!k || !v) return fail(SK_E_ARG, "k and v must be non-NULL");
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(SK_E_ARG, "k and v must be 16-byte aligned");
+    (void)hipGetLastError();
+    return device(sk::launch_upgrade_pack(dims(shape, n), m, k, v, tokens, payload,
+                                          (hipStream_t)stream),
+                  "upgrade pack");
+}
+
+sk_status sk_upgrade_unpack(const sk_shape* shape, int64_t n, const void* payload,
+                            const uint32_t* tokens, int64_t m, void* k_out, void* v_out,
+                            const sk_paged* paged, void* stream) {
+    if (sk_status st = check_upgrade(shape, n, m, tokens, payload)) return st;
+    if (paged) {
+        if (k_out || v_out) return fail(SK_E_ARG, "paged upgrade takes k_out = v_out = NULL");
+        if (paged->block_size < 1) return fail(SK_E_ARG, "block_size must be >= 1");
+        if (paged->num_blocks < (n + paged->block_size - 1) / paged->block_size)
+            return fail(SK_E_ARG, "num_blocks smaller than ceil(n / block_size)");
+    }
+    if (m == 0 || n == 0) return ok();
+    const sk::Dims d = dims(shape, n);
+    (void)hipGetLastError();
+    if (!paged) {
+        if (!k_out || !v_out) return fail(SK_E_ARG, "dense upgrade needs k_out and v_out");
+        if (!aligned(k_out, 16) || !aligned(v_out, 16))
+            return fail(SK_E_ARG, "k_out and v_out must be 16-byte aligned");
+        return device(sk::launch_upgrade_unpack(d, m, payload, tokens, k_out, v_out, nullptr, 1,
+                                                0, (hipStream_t)stream),
+                      "upgrade unpack");
+    }
+    if (!paged->k_cache || !paged->v_cache || !paged->block_table)
+        return fail(SK_E_ARG, "paged upgrade needs k_cache, v_cache and block_table");
+    if (!aligned(paged->k_cache, 16) || !aligned(paged->v_cache, 16) ||
+        !aligned(paged->block_table, 4))
+        return fail(SK_E_ARG, "paged caches must be 16-byte aligned, block_table 4-byte aligned");
+    return device(sk::launch_upgrade_unpack(d, m, payload, tokens, paged->k_cache,
+                                            paged->v_cache, paged->block_table,
+                                            paged->block_size, paged->num_blocks,
+                                            (hipStream_t)stream),
+                  "upgrade unpack");
+}
+
 }  // extern "C"

@@ -49,6 +49,14 @@ hipError_t launch_unpack_paged(const Dims& s, const TierSeg seg[3], const void* 
                                const int32_t* block_table, int32_t block_size,
                                int64_t num_blocks, hipStream_t st);
 
+// cold-tier upgrade: fp16 rows of m listed tokens (block_table NULL = dense)
+hipError_t launch_upgrade_pack(const Dims& s, int64_t m, const void* k, const void* v,
+                               const uint32_t* tokens, void* payload, hipStream_t st);
+hipError_t launch_upgrade_unpack(const Dims& s, int64_t m, const void* payload,
+                                 const uint32_t* tokens, void* k_out, void* v_out,
+                                 const int32_t* block_table, int32_t block_size,
+                                 int64_t num_blocks, hipStream_t st);
+
 // score variants: KV-norm fallback (score fp32 [n]) and recency weighting
 hipError_t launch_kvnorm(const Dims& s, const void* k, float* score, int accumulate,
                          hipStream_t st);

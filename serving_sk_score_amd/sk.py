@@ -23,7 +23,8 @@ EXPORTS = [
     "sk_plan_make", "sk_score_workspace_bytes", "sk_score", "sk_score_rowlse",
     "sk_score_colsum_workspace_bytes", "sk_score_colsum", "sk_assign_workspace_bytes",
     "sk_assign_tiers", "sk_pack", "sk_unpack", "sk_status_string", "sk_last_error",
-    "sk_layout_version", "sk_recency_weight", "sk_score_kvnorm",
+    "sk_layout_version", "sk_recency_weight", "sk_score_kvnorm", "sk_upgrade_bytes",
+    "sk_upgrade_pack", "sk_upgrade_unpack",
 ]
 
 
@@ -112,6 +113,9 @@ def lib():
             "sk_layout_version": (i32, []),
             "sk_recency_weight": (i32, [i64, ctypes.c_double, vp, vp, vp]),
             "sk_score_kvnorm": (i32, [P(_Shape), i64, vp, vp, i32, vp]),
+            "sk_upgrade_bytes": (sz, [P(_Shape), i64]),
+            "sk_upgrade_pack": (i32, [P(_Shape), i64, vp, vp, vp, i64, vp, vp]),
+            "sk_upgrade_unpack": (i32, [P(_Shape), i64, vp, vp, i64, vp, vp, P(_Paged), vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -299,4 +303,51 @@ def unpack_paged(shape: Shape, plan: Plan, payload, amap, k_cache, v_cache, bloc
     pg = _Paged(k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), block_size, nb)
     _check(lib().sk_unpack(ctypes.byref(shape.c()), ctypes.byref(plan.c), _ptr(payload),
                            _ptr(amap), None, None, ctypes.byref(pg), _stream(payload)))
+    return k_cache, v_cache
+
+
+def upgrade_bytes(shape: Shape, n_up: int) -> int:
+    return int(lib().sk_upgrade_bytes(ctypes.byref(shape.c()), n_up))
+
+
+def _tokens(tokens):
+    m = tokens.shape[0] if tokens.dim() == 1 else -1
+    _need(tokens, "tokens", torch.int32, shape=(m,))
+    return m
+
+
+def upgrade_pack(shape: Shape, k, v, tokens, payload):
+    """fp16 rows of the listed tokens (int32 [m], u32 bit patterns) into payload."""
+    n = k.shape[1] if k.dim() == 4 else -1
+    _need(k, "k", torch.float16, shape=_kv_shape(shape, n))
+    _need(v, "v", torch.float16, shape=_kv_shape(shape, n))
+    m = _tokens(tokens)
+    _need(payload, "payload", torch.uint8, numel=upgrade_bytes(shape, m))
+    _check(lib().sk_upgrade_pack(ctypes.byref(shape.c()), n, _ptr(k), _ptr(v), _ptr(tokens), m,
+                                 _ptr(payload), _stream(k)))
+    return payload
+
+
+def upgrade_unpack(shape: Shape, n: int, payload, tokens, k_out, v_out):
+    m = _tokens(tokens)
+    _need(payload, "payload", torch.uint8, numel=upgrade_bytes(shape, m))
+    _need(k_out, "k_out", torch.float16, shape=_kv_shape(shape, n))
+    _need(v_out, "v_out", torch.float16, shape=_kv_shape(shape, n))
+    _check(lib().sk_upgrade_unpack(ctypes.byref(shape.c()), n, _ptr(payload), _ptr(tokens), m,
+                                   _ptr(k_out), _ptr(v_out), None, _stream(payload)))
+    return k_out, v_out
+
+
+def upgrade_unpack_paged(shape: Shape, n: int, payload, tokens, k_cache, v_cache, block_table,
+                         block_size=16):
+    m = _tokens(tokens)
+    _need(payload, "payload", torch.uint8, numel=upgrade_bytes(shape, m))
+    nb = k_cache.shape[1] if k_cache.dim() == 5 else -1
+    cshape = (shape.n_layers, nb, block_size, shape.n_kv_heads, shape.head_dim)
+    _need(k_cache, "k_cache", torch.float16, shape=cshape)
+    _need(v_cache, "v_cache", torch.float16, shape=cshape)
+    _need(block_table, "block_table", torch.int32, numel=(n + block_size - 1) // block_size)
+    pg = _Paged(k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), block_size, nb)
+    _check(lib().sk_upgrade_unpack(ctypes.byref(shape.c()), n, _ptr(payload), _ptr(tokens), m,
+                                   None, None, ctypes.byref(pg), _stream(payload)))
     return k_cache, v_cache

@@ -154,6 +154,21 @@ def test_call_validation_without_device():
     assert lib.sk_score_kvnorm(B(shape), 10, FAKE, FAKE, 2, None) == sk.SK_E_ARG
     assert lib.sk_score_kvnorm(B(bad_shape), 10, FAKE, FAKE, 0, None) == sk.SK_E_UNSUPPORTED
     assert lib.sk_score_kvnorm(B(shape), 0, None, None, 0, None) == sk.SK_OK
+    # upgrade: sizes, NULLs, alignment, paged argument rules
+    assert lib.sk_upgrade_bytes(B(shape), 3) == 2 * 3 * 2 * 2 * 2 * 64
+    assert lib.sk_upgrade_bytes(B(shape), -1) == 0
+    assert lib.sk_upgrade_bytes(B(bad_shape), 3) == 0
+    assert lib.sk_upgrade_pack(B(shape), 100, FAKE, FAKE, None, 3, FAKE, None) == sk.SK_E_ARG
+    assert lib.sk_upgrade_pack(B(shape), 100, FAKE, FAKE, FAKE, 3, FAKE_MIS, None) == sk.SK_E_ARG
+    assert lib.sk_upgrade_pack(B(shape), 100, FAKE, FAKE, FAKE, -3, FAKE, None) == sk.SK_E_ARG
+    assert lib.sk_upgrade_pack(B(shape), 100, None, FAKE, FAKE, 3, FAKE, None) == sk.SK_E_ARG
+    assert lib.sk_upgrade_pack(B(shape), 100, None, None, None, 0, None, None) == sk.SK_OK
+    assert lib.sk_upgrade_unpack(B(shape), 100, FAKE, FAKE, 3, FAKE, None, None, None) == sk.SK_E_ARG
+    assert lib.sk_upgrade_unpack(B(shape), 100, FAKE, FAKE, 3, FAKE, FAKE, B(pg), None) == sk.SK_E_ARG
+    pg_ok = sk._Paged(0x7F0000001000, 0x7F0000001000, 0x7F0000001002, 16, 7)
+    assert lib.sk_upgrade_unpack(B(shape), 100, FAKE, FAKE, 3, None, None, B(pg_ok), None) == sk.SK_E_ARG
+    assert lib.sk_upgrade_unpack(B(shape), 100, FAKE, FAKE, 3, None, None, B(pg), None) == sk.SK_E_ARG
+    assert lib.sk_upgrade_unpack(B(shape), 100, None, None, 0, None, None, None, None) == sk.SK_OK
     empty = _plan((2, 4, 2, 64), (0, 4, 1, 0.5))
     assert lib.sk_pack(B(shape), B(empty.c), None, None, None, None, None, None) == sk.SK_OK
     assert lib.sk_unpack(B(shape), B(empty.c), None, None, None, None, None, None) == sk.SK_OK
