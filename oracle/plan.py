@@ -22,8 +22,16 @@ Readings where the pages leave a step open:
    extended to fp16/int8 (n16 = floor((Br - 2R)/2), n8 = R - n16), capped at
    n16 = R.
 4. A budget that cannot pay the cheapest allowed representation of every
-   token (3-tier: Br < R; 2-tier: Br < 2R) is rejected, never overrun.
-   Dropping tokens (§7.4.3) is a different policy and not modelled here.
+   token (3-tier: Br < R; 2-tier: Br < 2R) is rejected, never overrun, in
+   the default overflow mode REJECT.  Two other modes follow the pages'
+   other statements about that case:
+   - DROP (§7.4.3: at b = 0.3 a 2-tier policy can send only 60% of the
+     tokens, the rest are dropped): as many remaining tokens as Br pays at
+     the cheapest allowed tier are kept, floor(Br / cost); the lowest-ranked
+     rest are dropped (no bytes).  The sinks must still be paid (Br >= 0).
+   - FALLBACK (the Korean summary's tier table: below the low quantile a
+     token gets int4 when allowed, otherwise int8): every remaining token
+     goes at the cheapest allowed tier and the budget is overrun.
 5. Scale bytes are not charged to the budget (§2.1 uses nominal costs); they
    appear in the payload byte count.
 6. Payload layout (the pages define none): five segments
@@ -35,6 +43,8 @@ import math
 from dataclasses import dataclass
 
 FP16, INT8, INT4 = 0, 1, 2
+DROP = 3                                     # a dropped token: not sent
+REJECT, DROP_OVERFLOW, FALLBACK = 0, 1, 2    # budget overflow modes (reading 4)
 UNITS = {FP16: 4, INT8: 2, INT4: 1}          # §2.1 costs in quarter tokens
 
 
@@ -56,6 +66,7 @@ class Plan:
     off_c4: int
     off_s8: int
     off_s4: int
+    n_drop: int = 0     # tokens sent nowhere (overflow mode DROP)
 
 
 def fp16_bytes(L, H_kv, d, n):
@@ -68,15 +79,27 @@ def budget_units(b, n):
     return int(math.floor(4.0 * float(b) * float(n) + 1e-7))
 
 
-def tier_counts(n, S, b, three_tier):
-    """Return (N16, N8, N4, S') for one request (§4.4, §7.4.1, Algorithm 1)."""
+def tier_counts(n, S, b, three_tier, overflow=REJECT):
+    """Return (N16, N8, N4, S') for one request (§4.4, §7.4.1, Algorithm 1);
+    n - N16 - N8 - N4 tokens are dropped (only in overflow mode DROP)."""
     if n < 0 or S < 0:
         raise ValueError("n and S must be non-negative")
     if not (math.isfinite(b) and 0.0 <= b <= 1.0):
         raise ValueError("the budget b is a fraction of the fp16 bytes, 0 <= b <= 1")
+    if overflow not in (REJECT, DROP_OVERFLOW, FALLBACK):
+        raise ValueError("unknown overflow mode")
     s = min(S, n)
     R = n - s
     Br = budget_units(b, n) - 4 * s
+    cheapest = UNITS[INT4] if three_tier else UNITS[INT8]
+    if Br < cheapest * R and overflow != REJECT:
+        if overflow == FALLBACK:
+            kept = R
+        else:
+            if Br < 0:
+                raise BudgetError(f"budget pays {Br} quarter units after the sinks")
+            kept = Br // cheapest
+        return (s, 0, kept, s) if three_tier else (s, kept, 0, s)
     if three_tier:
         if Br < R:
             raise BudgetError(f"budget pays {Br} quarter units for {R} tokens")
@@ -93,11 +116,11 @@ def tier_counts(n, S, b, three_tier):
     return s + n16, n8, n4, s
 
 
-def make_plan(L, H_q, H_kv, d, n, S, b, three_tier):
+def make_plan(L, H_q, H_kv, d, n, S, b, three_tier, overflow=REJECT):
     """Counts plus the byte layout of the payload (reading 6)."""
     if d not in (64, 128, 256) or H_kv <= 0 or H_q % H_kv or L <= 0:
         raise ValueError("unsupported shape")
-    N16, N8, N4, s = tier_counts(n, S, b, three_tier)
+    N16, N8, N4, s = tier_counts(n, S, b, three_tier, overflow)
     rows16 = L * N16 * 2 * H_kv      # (layer, slot, K|V, head) rows per tier
     rows8 = L * N8 * 2 * H_kv
     rows4 = L * N4 * 2 * H_kv
@@ -111,7 +134,8 @@ def make_plan(L, H_q, H_kv, d, n, S, b, three_tier):
                 budget_units=budget_units(b, n),
                 used_units=4 * N16 + 2 * N8 + N4,
                 payload_bytes=total, off_c16=off_c16, off_c8=off_c8,
-                off_c4=off_c4, off_s8=off_s8, off_s4=off_s4)
+                off_c4=off_c4, off_s8=off_s8, off_s4=off_s4,
+                n_drop=n - N16 - N8 - N4)
 
 
 def bits_per_scalar(payload_bytes, L, H_kv, d, n):

@@ -167,12 +167,17 @@ def unpack_layer(payload, layer, amap, plan, H, d):
     return k, v
 
 
-def unpack_dense(payload, amap, plan, L, H, d):
+def unpack_dense(payload, amap, plan, L, H, d, K=None, V=None):
+    """Dequantized K, V [L][n][H][d].  Rows of dropped tokens (tier 3) are
+    not written: they keep the contents of K, V when given."""
     n = len(amap)
-    K = np.empty((L, n, H, d), dtype=np.float16)
-    V = np.empty((L, n, H, d), dtype=np.float16)
+    K = np.empty((L, n, H, d), dtype=np.float16) if K is None else K
+    V = np.empty((L, n, H, d), dtype=np.float16) if V is None else V
+    sent = _tiers(amap)[0] <= INT4
     for layer in range(L):
-        K[layer], V[layer] = unpack_layer(payload, layer, amap, plan, H, d)
+        k, v = unpack_layer(payload, layer, amap, plan, H, d)
+        K[layer, sent] = k[sent]
+        V[layer, sent] = v[sent]
     return K, V
 
 
@@ -182,10 +187,10 @@ def unpack_paged(payload, amap, plan, L, H, d, block_table, k_cache, v_cache,
     in place (reading 7)."""
     n = len(amap)
     bt = np.asarray(block_table, dtype=np.int64)
-    j = np.arange(n)
+    j = np.nonzero(_tiers(amap)[0] <= INT4)[0]          # dropped tokens: untouched
     blk = bt[j // block_size]
     pos = j % block_size
     for layer in range(L):
         k, v = unpack_layer(payload, layer, amap, plan, H, d)
-        k_cache[layer, blk, pos] = k
-        v_cache[layer, blk, pos] = v
+        k_cache[layer, blk, pos] = k[j]
+        v_cache[layer, blk, pos] = v[j]

@@ -95,3 +95,53 @@ def test_negative_zero_is_zero():
 def test_rejects_nonfinite():
     with pytest.raises(AssertionError):
         A.assign(np.array([1.0, np.nan], dtype=np.float32), 1, 1, 0, 0)
+
+
+# ------------------------------------------------- drops and variants --
+
+def test_dropped_tokens_are_the_lowest_ranked():
+    rng = np.random.default_rng(12)
+    for trial in range(30):
+        n = int(rng.integers(1, 300))
+        S = int(rng.integers(0, min(n, 6) + 1))
+        sc = (rng.integers(0, 20, size=n) * 0.25).astype(np.float32)   # many ties
+        n16 = S + int(rng.integers(0, n - S + 1))
+        n8 = int(rng.integers(0, n - n16 + 1))
+        n4 = int(rng.integers(0, n - n16 - n8 + 1))
+        tier, slot, amap, order = A.assign(sc, n16, n8, n4, S)
+        # brute force with Python's sort: rank by (score desc, index asc)
+        ranked = sorted(range(S, n), key=lambda j: (-float(sc[j]), j))
+        want = [0] * S + [None] * (n - S)
+        cuts = [n16 - S, n16 - S + n8, n16 - S + n8 + n4]
+        for r, j in enumerate(ranked):
+            want[j] = 0 if r < cuts[0] else 1 if r < cuts[1] else 2 if r < cuts[2] else 3
+        assert list(tier) == want, trial
+        assert np.sum(tier == 3) == n - n16 - n8 - n4
+        # dropped tokens take slots in token order and close the order list
+        drop = np.nonzero(tier == 3)[0]
+        assert list(slot[drop]) == list(range(len(drop)))
+        assert list(order[n - len(drop):]) == list(drop)
+        assert np.all((amap >> 30)[drop] == 3)
+
+
+def test_balanced_power_of_two_is_strided():
+    keys = A.balanced_keys(64 + 3, 3)                 # 3 sinks, R = 64
+    assert np.all(keys[:3] == 0)
+    tier, _, _, _ = A.assign(keys, 3 + 16, 16, 32, 3)
+    r = np.arange(64)
+    assert np.array_equal(np.nonzero(tier[3:] == 0)[0], r[r % 4 == 0])
+    assert np.array_equal(np.nonzero(tier[3:] <= 1)[0], r[r % 2 == 0])
+
+
+def test_balanced_spreads_every_tier_boundary():
+    for R in (5, 100, 1000, 1025):
+        keys = A.balanced_keys(R, 0)
+        assert len(np.unique(keys)) == R                  # a strict ranking, no ties
+        b = int(np.ceil(np.log2(R)))
+        order = sorted(range(R), key=lambda j: -float(keys[j]))
+        w = np.arange(1, R + 1)
+        for k in range(1, R, max(1, R // 50)):
+            sel = np.zeros(R, dtype=bool)
+            sel[order[:k]] = True
+            dev = np.max(np.abs(np.cumsum(sel) - w * k / R))
+            assert dev <= b / 2, (R, k, dev)              # position-greedy would be ~k(R-k)/R

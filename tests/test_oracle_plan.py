@@ -16,6 +16,7 @@ import itertools
 import math
 from fractions import Fraction
 
+import numpy as np
 import pytest
 
 from oracle import plan as P
@@ -178,3 +179,51 @@ def test_domain_errors():
 def test_empty_request():
     pl = P.make_plan(2, 4, 2, 64, 0, 4, 0.5, 1)
     assert (pl.n16, pl.n8, pl.n4, pl.payload_bytes) == (0, 0, 0, 0)
+
+
+# ------------------------------------------------------- overflow modes --
+# Reading 4: REJECT (default), DROP (§7.4.3: a 2-tier policy at b = 0.3 sends
+# only 60% of the tokens) and FALLBACK (the Korean summary's tier table: the
+# lowest band gets int4 if allowed, else int8, whatever the budget).
+
+def test_drop_mode_page_example():
+    n = 1000
+    N16, N8, N4, s = P.tier_counts(n, 0, 0.3, 0, P.DROP_OVERFLOW)
+    assert (N16, N8, N4, s) == (0, 600, 0, 0)             # 60% of the tokens sent
+    plan = P.make_plan(1, 4, 2, 64, n, 0, 0.3, 0, P.DROP_OVERFLOW)
+    assert plan.n_drop == 400 and plan.used_units <= plan.budget_units
+
+
+def test_drop_mode_three_tier_and_sinks():
+    N16, N8, N4, s = P.tier_counts(1000, 4, 0.2, 1, P.DROP_OVERFLOW)
+    # B = 800, sinks take 16, 784 int4 tokens of the 996 others
+    assert (N16, N8, N4, s) == (4, 0, 784, 4)
+    with pytest.raises(P.BudgetError):                    # the sinks alone overrun
+        P.tier_counts(100, 30, 0.2, 1, P.DROP_OVERFLOW)
+    # an odd unit left over stays unused in 2-tier
+    N16, N8, N4, _ = P.tier_counts(10, 1, 0.33, 0, P.DROP_OVERFLOW)
+    assert (N16, N8, N4) == (1, 4, 0)                      # B = 13, Br = 9 -> 4 int8
+
+
+def test_fallback_mode_overruns():
+    N16, N8, N4, s = P.tier_counts(1000, 4, 0.3, 0, P.FALLBACK)
+    assert (N16, N8, N4) == (4, 996, 0)
+    plan = P.make_plan(2, 4, 2, 64, 1000, 4, 0.3, 0, P.FALLBACK)
+    assert plan.used_units == 16 + 2 * 996 > plan.budget_units and plan.n_drop == 0
+    N16, N8, N4, s = P.tier_counts(1000, 4, 0.1, 1, P.FALLBACK)
+    assert (N16, N8, N4) == (4, 0, 996)
+
+
+def test_modes_agree_when_the_budget_suffices():
+    rng = np.random.default_rng(9)
+    for _ in range(300):
+        n = int(rng.integers(0, 3000))
+        S = int(rng.integers(0, 8))
+        b = float(rng.random())
+        three = int(rng.integers(0, 2))
+        try:
+            want = P.tier_counts(n, S, b, three)
+        except P.BudgetError:
+            continue
+        for mode in (P.DROP_OVERFLOW, P.FALLBACK):
+            assert P.tier_counts(n, S, b, three, mode) == want
