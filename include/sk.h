@@ -54,6 +54,7 @@ typedef int32_t sk_status;
 #define SK_TIER_FP16 0u
 #define SK_TIER_INT8 1u
 #define SK_TIER_INT4 2u
+#define SK_TIER_DROP 3u   /* not sent (overflow mode SK_OVERFLOW_DROP) */
 #define SK_MAP_TIER(m) ((uint32_t)(m) >> 30)
 #define SK_MAP_SLOT(m) ((uint32_t)(m) & 0x3FFFFFFFu)
 
@@ -68,16 +69,33 @@ typedef struct {
     int32_t head_dim;
 } sk_shape;
 
+/* What to do when the budget cannot pay every non-sink token at the
+ * cheapest allowed tier (int4 in 3-tier, int8 in 2-tier):
+ *   SK_OVERFLOW_REJECT   : sk_plan_make fails with SK_E_BUDGET (default)
+ *   SK_OVERFLOW_DROP     : §7.4.3 (a 2-tier policy at b = 0.3 sends only 60%
+ *                          of the tokens): floor(Br / cost) tokens are sent
+ *                          at the cheapest tier and the lowest-ranked rest
+ *                          are dropped (tier SK_TIER_DROP, no bytes); the
+ *                          sinks must still fit (Br >= 0, else SK_E_BUDGET)
+ *   SK_OVERFLOW_FALLBACK : the tier table of the Korean SpectrumKV summary
+ *                          (lowest band int4 when allowed, else int8): every
+ *                          token is sent at the cheapest tier, over budget */
+#define SK_OVERFLOW_REJECT   0
+#define SK_OVERFLOW_DROP     1
+#define SK_OVERFLOW_FALLBACK 2
+
 /* Transfer policy of one request.
  *   n_tokens   : n, 0 <= n < 2^30
  *   n_sink     : S >= 0, leading tokens pinned to fp16 (§7.4.1)
  *   three_tier : 1 = fp16/int8/int4 (int4 probe passed, §4.5), 0 = fp16/int8
- *   budget     : b in [0, 1], fraction of the fp16 bytes (§2.1, §4.4) */
+ *   budget     : b in [0, 1], fraction of the fp16 bytes (§2.1, §4.4)
+ *   overflow   : one of SK_OVERFLOW_* (zero-initialised policies reject) */
 typedef struct {
     int64_t n_tokens;
     int32_t n_sink;
     int32_t three_tier;
     double  budget;
+    int32_t overflow;
 } sk_policy;
 
 /* Tier counts and payload layout, a pure function of (shape, policy).
@@ -90,6 +108,9 @@ typedef struct {
  *           n16 = min(R, floor((Br - 2R)/2)), n8 = R - n16, n4 = 0.
  *   2-tier: Br < 2R -> SK_E_BUDGET; otherwise as the upper 3-tier branch.
  *   N16 = S' + n16, N8 = n8, N4 = n4.
+ *   The SK_E_BUDGET cases above become, with overflow = SK_OVERFLOW_DROP,
+ *   N4 (3-tier) or N8 (2-tier) = floor(Br / cost) and N_drop = R minus that,
+ *   and with SK_OVERFLOW_FALLBACK, N4 or N8 = R (used_units > budget_units).
  *
  * Payload layout v1 (no padding): segments c16 | c8 | c4 | s8 | s4.
  *   A "row" is (layer l, slot, kv in {0 = K, 1 = V}, KV head g) of head_dim
@@ -102,6 +123,7 @@ typedef struct {
  *   payload_bytes = L * 2H * (N16 * 2d + N8 * (d + 2) + N4 * (d/2 + 2)). */
 typedef struct {
     int64_t n16, n8, n4;        /* n16 includes the sinks */
+    int64_t n_drop;             /* tokens not sent: n = n16 + n8 + n4 + n_drop */
     int64_t n_sink;             /* S' */
     int64_t budget_units;       /* B */
     int64_t used_units;         /* 4 N16 + 2 N8 + N4 <= B */
@@ -116,7 +138,7 @@ typedef struct {
 
 /* Host only, pure, touches no device.  Returns SK_E_ARG / SK_E_UNSUPPORTED
  * for a bad shape or policy and SK_E_BUDGET when the budget cannot pay every
- * token (out is then left untouched). */
+ * token under the policy's overflow mode (out is then left untouched). */
 sk_status sk_plan_make(const sk_shape* shape, const sk_policy* policy, sk_plan* out);
 
 /* ---------------------------------------------------------------- score --
@@ -190,15 +212,28 @@ sk_status sk_score_kvnorm(const sk_shape* shape, int64_t n_tokens, const void* k
  * Tier assignment (§7.4.1 sinks, §2.3 sorted assignment, §4.4 counts):
  * tokens j < S' get fp16; the others are ranked by (score descending, token
  * index ascending) - ties go to the lower index - and the first n16 - S'
- * take fp16, the next n8 int8 and the rest int4.
+ * take fp16, the next n8 int8, the next n4 int4 and the rest (n_drop) are
+ * dropped (SK_TIER_DROP; pack and unpack skip them).
+ *
+ * Assignment-only variants (§7 baselines, §7.4.1 Table 11, §7.4.2 Table 12)
+ * rank by another key passed as `score`: Random_Tier keeps the tier counts
+ * and ranks by caller-drawn i.i.d. random keys; Balanced ranks by the keys
+ * of sk_balanced_keys, which spread every tier evenly over the positions
+ * regardless of importance.
  *   score : fp32 [n], finite and >= 0 (-0.0 counts as +0.0; NaN/Inf: the
  *           output is unspecified but every write stays in bounds)
  *   map   : u32 [n], map[j] = tier << 30 | slot, slot = number of tokens
  *           j' < j with the same tier
  *   order : u32 [n], the tokens sorted by (tier, index): fp16 slots first,
- *           then int8, then int4; order[off_t + slot] = j
+ *           then int8, then int4, then dropped; order[off_t + slot] = j
  *   ws    : at least sk_assign_workspace_bytes(n) bytes. */
 size_t    sk_assign_workspace_bytes(int64_t n_tokens);
+/* Balanced keys: keys[j] = 0 for j < S' = min(n_sink, n); for the others,
+ * with r = j - S', R = n - S' and b the fewest bits that hold R - 1,
+ * keys[j] = 2^b - 1 - bitreverse_b(r) (fp32, exact): ranking by it visits
+ * the positions in van der Corput order, so the tokens of every tier are
+ * spread evenly over the sequence.  R > 2^24 -> SK_E_UNSUPPORTED. */
+sk_status sk_balanced_keys(int64_t n_tokens, int32_t n_sink, float* keys, void* stream);
 sk_status sk_assign_tiers(const sk_policy* policy, const sk_plan* plan,
                           const float* score, uint32_t* map, uint32_t* order,
                           void* ws, size_t ws_bytes, void* stream);
@@ -225,7 +260,8 @@ sk_status sk_pack(const sk_shape* shape, const sk_plan* plan,
  * Decode side (§4.2): x_hat = fp16_rne(float(q) * float(s)) for int rows,
  * the raw fp16 row otherwise.
  * Dense:  paged == NULL, k_out / v_out fp16 [n_layers][n][n_kv_heads][head_dim]
- *         (every element written).
+ *         (every element written, except the rows of dropped tokens, which
+ *         are left untouched; attention must mask those tokens out).
  * Paged:  k_out = v_out = NULL; token j of layer l is written to
  *         cache[l][block_table[j / block_size]][j % block_size][g][:] of
  *         k_cache and v_cache, both fp16

@@ -7,17 +7,19 @@
 // importance-weighted error for fixed counts.  Ties go to the lower token
 // index.
 //
-// Method.  A token's rank only matters through two thresholds: the k1-th and
-// the k2-th largest key among the non-sink tokens, k1 = n16 - S', k2 = k1 + n8.
+// Method.  A token's rank only matters through three thresholds: the k1-th,
+// k2-th and k3-th largest key among the non-sink tokens, k1 = n16 - S',
+// k2 = k1 + n8, k3 = k2 + n4 (k3 < R only when the plan drops tokens).
 // Keys are unique integers key = (score bits << b) | (2^b - 1 - j), where
 // b = bits needed to hold n, so a larger key means a higher score or, on a
 // tie, a lower index; for non-negative floats the IEEE bit pattern is
-// monotone.  Both thresholds are found with one MSB-first radix select
-// (8-bit digits, LDS histograms, one workgroup) - each pass narrows the
-// prefix of both thresholds at once.  A token is fp16 iff key >= K_k1, int8
-// iff not fp16 and key >= K_k2, int4 otherwise.  Slots (positions among the
-// same tier in token order) come from wavefront ballots and a workgroup
-// prefix over 1024-token tiles; order[] is the inverse permutation.
+// monotone.  The thresholds strictly inside (0, R) are found with one
+// MSB-first radix select (8-bit digits, LDS histograms, one workgroup) - each
+// pass narrows the prefixes of all of them at once.  A token is fp16 iff
+// key >= K_k1, else int8 iff key >= K_k2, else int4 iff key >= K_k3, else
+// dropped.  Slots (positions among the same tier in token order) come from
+// wavefront ballots and a workgroup prefix over 1024-token tiles; order[] is
+// the inverse permutation, dropped tokens last.
 //
 // Histogram contention: the top digits of nearby scores coincide, so every
 // thread first merges runs of equal digits in registers and issues one LDS
@@ -82,14 +84,16 @@ __device__ void find_digit(const uint32_t* hist, uint64_t k, int lane, int* out_
 
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ score, int64_t n, int64_t sinks, int64_t k1, int64_t k2,
-    int64_t n16, int64_t n8, uint32_t* __restrict__ map, uint32_t* __restrict__ order) {
-    __shared__ uint32_t hist[2][256];
-    __shared__ uint64_t prefix[2];
-    __shared__ uint64_t krem[2];
-    __shared__ int sel_digit[2];
-    __shared__ uint64_t sel_above[2];
-    __shared__ uint32_t wcnt[kWaves][3];
-    __shared__ uint32_t running[3];
+    int64_t k3, int64_t n16, int64_t n8, int64_t n4, uint32_t* __restrict__ map,
+    uint32_t* __restrict__ order) {
+    constexpr int NS = 3;  // thresholds
+    __shared__ uint32_t hist[NS][256];
+    __shared__ uint64_t prefix[NS];
+    __shared__ uint64_t krem[NS];
+    __shared__ int sel_digit[NS];
+    __shared__ uint64_t sel_above[NS];
+    __shared__ uint32_t wcnt[kWaves][4];
+    __shared__ uint32_t running[4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -101,54 +105,59 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const int total_bits = 32 + bits;
     const int passes = (total_bits + 7) / 8;
 
-    // selection s in {0, 1} is active when 1 <= k_s <= R
-    const int64_t ks[2] = {k1, k2};
-    bool active[2];
-    for (int s = 0; s < 2; ++s) active[s] = ks[s] >= 1 && ks[s] <= R;
+    // cond_s(key) = rank < k_s: false for k_s <= 0, true for k_s >= R, else
+    // a radix-selected threshold
+    const int64_t ks[NS] = {k1, k2, k3};
+    bool active[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) active[s] = ks[s] >= 1 && ks[s] < R;
     if (tid == 0) {
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < NS; ++s) {
             prefix[s] = 0;
             krem[s] = (uint64_t)(active[s] ? ks[s] : 1);
         }
     }
+    const bool any = active[0] || active[1] || active[2];
     uint64_t pmask = 0;  // bits of the key fixed so far (uniform)
 
-    for (int p = 0; p < passes && (active[0] || active[1]); ++p) {
+    for (int p = 0; p < passes && any; ++p) {
         const int shift = 8 * (passes - 1 - p);
-        for (int i = tid; i < 512; i += kThreads) (&hist[0][0])[i] = 0;
+        for (int i = tid; i < NS * 256; i += kThreads) (&hist[0][0])[i] = 0;
         __syncthreads();
-        const uint64_t pre0 = prefix[0], pre1 = prefix[1];
-        int run_d0 = -1, run_d1 = -1;
-        uint32_t run_c0 = 0, run_c1 = 0;
+        uint64_t pre[NS];
+        int run_d[NS];
+        uint32_t run_c[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            pre[s] = prefix[s];
+            run_d[s] = -1;
+            run_c[s] = 0;
+        }
         for (int64_t j = sinks + tid; j < n; j += kThreads) {
             const uint64_t key = make_key(score[j], j, bits);
             const int dg = (int)((key >> shift) & 0xFFu);
-            if (active[0] && (key & pmask) == pre0) {
-                if (dg != run_d0) {
-                    if (run_c0) atomicAdd(&hist[0][run_d0], run_c0);
-                    run_d0 = dg;
-                    run_c0 = 0;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (active[s] && (key & pmask) == pre[s]) {
+                    if (dg != run_d[s]) {
+                        if (run_c[s]) atomicAdd(&hist[s][run_d[s]], run_c[s]);
+                        run_d[s] = dg;
+                        run_c[s] = 0;
+                    }
+                    ++run_c[s];
                 }
-                ++run_c0;
-            }
-            if (active[1] && (key & pmask) == pre1) {
-                if (dg != run_d1) {
-                    if (run_c1) atomicAdd(&hist[1][run_d1], run_c1);
-                    run_d1 = dg;
-                    run_c1 = 0;
-                }
-                ++run_c1;
             }
         }
-        if (run_c0) atomicAdd(&hist[0][run_d0], run_c0);
-        if (run_c1) atomicAdd(&hist[1][run_d1], run_c1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (run_c[s]) atomicAdd(&hist[s][run_d[s]], run_c[s]);
         __syncthreads();
-        if (wave < 2 && active[wave]) {
+        if (wave < NS && active[wave]) {
             find_digit(hist[wave], krem[wave], lane, &sel_digit[wave], &sel_above[wave]);
         }
         __syncthreads();
         if (tid == 0) {
-            for (int s = 0; s < 2; ++s) {
+            for (int s = 0; s < NS; ++s) {
                 if (!active[s]) continue;
                 prefix[s] |= (uint64_t)sel_digit[s] << shift;
                 krem[s] -= sel_above[s];
@@ -158,12 +167,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         __syncthreads();
     }
 
-    const uint64_t K1 = prefix[0], K2 = prefix[1];
-    // cond_s(key): rank < k_s  (k_s = 0 -> false, k_s > R -> true)
-    const bool all1 = k1 > R, none1 = k1 <= 0;
-    const bool all2 = k2 > R, none2 = k2 <= 0;
-    const uint32_t base[3] = {0u, (uint32_t)n16, (uint32_t)(n16 + n8)};
-    if (tid < 3) running[tid] = 0;
+    uint64_t K[NS];
+    bool all[NS], none[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        K[s] = prefix[s];
+        all[s] = ks[s] >= R;
+        none[s] = ks[s] <= 0;
+    }
+    const uint32_t base[4] = {0u, (uint32_t)n16, (uint32_t)(n16 + n8),
+                              (uint32_t)(n16 + n8 + n4)};
+    if (tid < 4) running[tid] = 0;
     __syncthreads();
     for (int64_t t0 = 0; t0 < n; t0 += kThreads) {
         const int64_t j = t0 + tid;
@@ -173,14 +187,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
                 tier = 0;
             } else {
                 const uint64_t key = make_key(score[j], j, bits);
-                const bool c1 = !none1 && (all1 || key >= K1);
-                const bool c2 = !none2 && (all2 || key >= K2);
-                tier = c1 ? 0 : (c2 ? 1 : 2);
+                tier = 3;
+#pragma unroll
+                for (int s = NS - 1; s >= 0; --s)
+                    if (!none[s] && (all[s] || key >= K[s])) tier = s;
             }
         }
         uint32_t mypre = 0;
 #pragma unroll
-        for (int t = 0; t < 3; ++t) {
+        for (int t = 0; t < 4; ++t) {
             const unsigned long long b = __ballot(tier == t);
             if (lane == 0) wcnt[wave][t] = (uint32_t)__popcll(b);
             if (tier == t) mypre = (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
             order[base[tier] + slot] = (uint32_t)j;
         }
         __syncthreads();
-        if (tid < 3) {
+        if (tid < 4) {
             uint32_t s = 0;
             for (int w = 0; w < kWaves; ++w) s += wcnt[w][tid];
             running[tid] += s;
@@ -203,16 +218,40 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
 }
 
+// Balanced ranking key of the non-sink token at offset r = j - sinks:
+// 2^b - 1 - bitreverse_b(r), b = fewest bits that hold R - 1 (exact in fp32
+// for R <= 2^24); sinks get 0.
+__global__ __launch_bounds__(256) void balanced_kernel(float* __restrict__ keys, int64_t n,
+                                                       int64_t sinks, int b) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= n) return;
+    if (j < sinks) {
+        keys[j] = 0.0f;
+        return;
+    }
+    const uint32_t r = (uint32_t)(j - sinks);
+    const uint32_t rev = b ? (__builtin_bitreverse32(r) >> (32 - b)) : 0u;
+    keys[j] = (float)(((1u << b) - 1u) - rev);
+}
+
 }  // namespace
 
 hipError_t launch_select(int64_t n, int64_t sinks, int64_t n16, int64_t n8, int64_t n4,
                          const float* score, uint32_t* map, uint32_t* order,
                          hipStream_t st) {
-    (void)n4;
     const int64_t k1 = n16 - sinks;
     const int64_t k2 = k1 + n8;
+    const int64_t k3 = k2 + n4;
     hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kThreads), 0, st, score, n, sinks, k1, k2,
-                       n16, n8, map, order);
+                       k3, n16, n8, n4, map, order);
+    return hipGetLastError();
+}
+
+hipError_t launch_balanced(int64_t n, int64_t sinks, float* keys, hipStream_t st) {
+    int b = 0;
+    while (((int64_t)1 << b) < n - sinks) ++b;
+    hipLaunchKernelGGL(balanced_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, keys,
+                       n, sinks, b);
     return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ sk_status check_tokens(int64_t n) {
 }
 
 uint64_t plan_hash(const sk_plan& p) {
-    const int64_t f[] = {p.n16, p.n8, p.n4, p.n_sink, p.budget_units, p.used_units,
+    const int64_t f[] = {p.n16, p.n8, p.n4, p.n_drop, p.n_sink, p.budget_units, p.used_units,
                          p.payload_bytes, p.off_c16, p.off_c8, p.off_c4, p.off_s8, p.off_s4,
                          p.n_tokens, p.n_layers, p.n_kv_heads, p.head_dim, p.layout_version};
     uint64_t h = 1469598103934665603ull;  // FNV-1a
@@ -134,6 +134,9 @@ sk_status sk_plan_make(const sk_shape* shape, const sk_policy* pol, sk_plan* out
         return fail(SK_E_ARG, "three_tier must be 0 or 1");
     if (!std::isfinite(pol->budget) || pol->budget < 0.0 || pol->budget > 1.0)
         return fail(SK_E_ARG, "budget must be a finite fraction in [0, 1]");
+    if (pol->overflow != SK_OVERFLOW_REJECT && pol->overflow != SK_OVERFLOW_DROP &&
+        pol->overflow != SK_OVERFLOW_FALLBACK)
+        return fail(SK_E_ARG, "overflow must be one of SK_OVERFLOW_*");
 
     const int64_t n = pol->n_tokens;
     const int64_t S = pol->n_sink < n ? pol->n_sink : n;
@@ -142,7 +145,17 @@ sk_status sk_plan_make(const sk_shape* shape, const sk_policy* pol, sk_plan* out
     const int64_t B = (int64_t)std::floor(4.0 * pol->budget * (double)n + 1e-7);
     const int64_t Br = B - 4 * S;
     int64_t n16 = 0, n8 = 0, n4 = 0;
-    if (pol->three_tier) {
+    const int64_t cheapest = pol->three_tier ? 1 : 2;  // units of the cheapest tier
+    if (Br < cheapest * R && pol->overflow != SK_OVERFLOW_REJECT) {
+        int64_t kept = R;
+        if (pol->overflow == SK_OVERFLOW_DROP) {
+            if (Br < 0)
+                return fail(SK_E_BUDGET, "budget %.6g does not pay the %lld sinks", pol->budget,
+                            (long long)S);
+            kept = Br / cheapest;
+        }
+        (pol->three_tier ? n4 : n8) = kept;
+    } else if (pol->three_tier) {
         if (Br < R)
             return fail(SK_E_BUDGET, "budget %.6g pays %lld quarter units for %lld tokens",
                         pol->budget, (long long)Br, (long long)R);
@@ -167,6 +180,7 @@ sk_status sk_plan_make(const sk_shape* shape, const sk_policy* pol, sk_plan* out
     p.n16 = S + n16;
     p.n8 = n8;
     p.n4 = n4;
+    p.n_drop = R - n16 - n8 - n4;
     p.n_sink = S;
     p.budget_units = B;
     p.used_units = 4 * p.n16 + 2 * p.n8 + p.n4;
@@ -287,6 +301,19 @@ sk_status sk_score_kvnorm(const sk_shape* shape, int64_t n, const void* k, float
     (void)hipGetLastError();
     return device(sk::launch_kvnorm(dims(shape, n), k, score, accumulate, (hipStream_t)stream),
                   "kvnorm");
+}
+
+sk_status sk_balanced_keys(int64_t n, int32_t n_sink, float* keys, void* stream) {
+    if (sk_status st = check_tokens(n)) return st;
+    if (n_sink < 0) return fail(SK_E_ARG, "n_sink must be >= 0");
+    const int64_t S = n_sink < n ? n_sink : n;
+    if (n - S > ((int64_t)1 << 24))
+        return fail(SK_E_UNSUPPORTED, "balanced keys are exact in fp32 for at most 2^24 tokens");
+    if (n == 0) return ok();
+    if (!keys) return fail(SK_E_ARG, "keys must be non-NULL");
+    if (!aligned(keys, 4)) return fail(SK_E_ARG, "keys must be 4-byte aligned");
+    (void)hipGetLastError();
+    return device(sk::launch_balanced(n, S, keys, (hipStream_t)stream), "balanced keys");
 }
 
 size_t sk_assign_workspace_bytes(int64_t n) {

@@ -33,7 +33,10 @@ int64_t padded_tokens(int64_t n);
 // number of rows of the pass-2 partial buffer
 int colsum_partial_rows(const Dims& s);
 
-// tier selection
+// Balanced-variant ranking keys (fp32 [n], n - sinks <= 2^24)
+hipError_t launch_balanced(int64_t n, int64_t sinks, float* keys, hipStream_t st);
+
+// tier selection (n16 + n8 + n4 <= n; the lowest-ranked rest get tier 3)
 hipError_t launch_select(int64_t n, int64_t sinks, int64_t n16, int64_t n8, int64_t n4,
                          const float* score, uint32_t* map, uint32_t* order,
                          hipStream_t st);

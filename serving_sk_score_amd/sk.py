@@ -17,14 +17,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsk.so")
 
 SK_OK, SK_E_ARG, SK_E_UNSUPPORTED, SK_E_BUDGET, SK_E_WORKSPACE, SK_E_DEVICE = range(6)
-TIER_FP16, TIER_INT8, TIER_INT4 = 0, 1, 2
+TIER_FP16, TIER_INT8, TIER_INT4, TIER_DROP = 0, 1, 2, 3
+OVERFLOW_REJECT, OVERFLOW_DROP, OVERFLOW_FALLBACK = 0, 1, 2
 
 EXPORTS = [
     "sk_plan_make", "sk_score_workspace_bytes", "sk_score", "sk_score_rowlse",
     "sk_score_colsum_workspace_bytes", "sk_score_colsum", "sk_assign_workspace_bytes",
     "sk_assign_tiers", "sk_pack", "sk_unpack", "sk_status_string", "sk_last_error",
     "sk_layout_version", "sk_recency_weight", "sk_score_kvnorm", "sk_upgrade_bytes",
-    "sk_upgrade_pack", "sk_upgrade_unpack",
+    "sk_upgrade_pack", "sk_upgrade_unpack", "sk_balanced_keys",
 ]
 
 
@@ -41,12 +42,13 @@ class _Shape(ctypes.Structure):
 
 class _Policy(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int64), ("n_sink", ctypes.c_int32),
-                ("three_tier", ctypes.c_int32), ("budget", ctypes.c_double)]
+                ("three_tier", ctypes.c_int32), ("budget", ctypes.c_double),
+                ("overflow", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
     _fields_ = [("n16", ctypes.c_int64), ("n8", ctypes.c_int64), ("n4", ctypes.c_int64),
-                ("n_sink", ctypes.c_int64), ("budget_units", ctypes.c_int64),
+                ("n_drop", ctypes.c_int64), ("n_sink", ctypes.c_int64), ("budget_units", ctypes.c_int64),
                 ("used_units", ctypes.c_int64), ("payload_bytes", ctypes.c_int64),
                 ("off_c16", ctypes.c_int64), ("off_c8", ctypes.c_int64),
                 ("off_c4", ctypes.c_int64), ("off_s8", ctypes.c_int64),
@@ -79,9 +81,11 @@ class Policy:
     n_sink: int
     three_tier: int
     budget: float
+    overflow: int = OVERFLOW_REJECT
 
     def c(self):
-        return _Policy(self.n_tokens, self.n_sink, self.three_tier, float(self.budget))
+        return _Policy(self.n_tokens, self.n_sink, self.three_tier, float(self.budget),
+                       self.overflow)
 
 
 _lib = None
@@ -114,6 +118,7 @@ def lib():
             "sk_recency_weight": (i32, [i64, ctypes.c_double, vp, vp, vp]),
             "sk_score_kvnorm": (i32, [P(_Shape), i64, vp, vp, i32, vp]),
             "sk_upgrade_bytes": (sz, [P(_Shape), i64]),
+            "sk_balanced_keys": (i32, [i64, i32, vp, vp]),
             "sk_upgrade_pack": (i32, [P(_Shape), i64, vp, vp, vp, i64, vp, vp]),
             "sk_upgrade_unpack": (i32, [P(_Shape), i64, vp, vp, i64, vp, vp, P(_Paged), vp]),
         }
@@ -246,6 +251,13 @@ def score_kvnorm(shape: Shape, k, out, accumulate=False):
     _check(lib().sk_score_kvnorm(ctypes.byref(shape.c()), n, _ptr(k), _ptr(out),
                                  int(bool(accumulate)), _stream(k)))
     return out
+
+
+def balanced_keys(n: int, n_sink: int, keys):
+    """Ranking keys of the Balanced variant into keys (fp32 [n])."""
+    _need(keys, "keys", torch.float32, shape=(n,))
+    _check(lib().sk_balanced_keys(n, n_sink, _ptr(keys), _stream(keys)))
+    return keys
 
 
 def assign_tiers(policy: Policy, plan: Plan, score_t, amap, order, ws=None):

@@ -40,9 +40,9 @@ def test_layout_version_and_strings():
     assert b"unknown" in lib.sk_status_string(99)
 
 
-def _oracle_or_err(L, Hq, H, d, n, S, b, three):
+def _oracle_or_err(L, Hq, H, d, n, S, b, three, overflow=0):
     try:
-        return OP.make_plan(L, Hq, H, d, n, S, b, three)
+        return OP.make_plan(L, Hq, H, d, n, S, b, three, overflow)
     except OP.BudgetError:
         return "budget"
 
@@ -56,16 +56,19 @@ def test_plan_parity_random():
         S = rnd.choice([0, 1, 4, 32])
         b = rnd.choice([0.0, 0.25, 0.3, 0.5, 0.6, 0.7, 1.0, round(rnd.random(), 4)])
         three = rnd.choice([0, 1])
-        want = _oracle_or_err(L, Hq, H, d, n, S, b, three)
+        mode = rnd.choice([sk.OVERFLOW_REJECT, sk.OVERFLOW_DROP, sk.OVERFLOW_FALLBACK])
+        assert (OP.REJECT, OP.DROP_OVERFLOW, OP.FALLBACK) == (0, 1, 2)
+        want = _oracle_or_err(L, Hq, H, d, n, S, b, three, mode)
+        pol = sk.Policy(n, S, three, b, mode)
         if want == "budget":
             with pytest.raises(sk.SkError) as e:
-                sk.plan_make(sk.Shape(L, Hq, H, d), sk.Policy(n, S, three, b))
+                sk.plan_make(sk.Shape(L, Hq, H, d), pol)
             assert e.value.status == sk.SK_E_BUDGET
             continue
-        got = sk.plan_make(sk.Shape(L, Hq, H, d), sk.Policy(n, S, three, b))
-        for f in ("n16", "n8", "n4", "budget_units", "used_units", "payload_bytes",
+        got = sk.plan_make(sk.Shape(L, Hq, H, d), pol)
+        for f in ("n16", "n8", "n4", "n_drop", "budget_units", "used_units", "payload_bytes",
                   "off_c16", "off_c8", "off_c4", "off_s8", "off_s4"):
-            assert getattr(got, f) == getattr(want, f), (f, L, Hq, H, d, n, S, b, three)
+            assert getattr(got, f) == getattr(want, f), (f, L, Hq, H, d, n, S, b, three, mode)
         assert got.n_sink == want.sinks
 
 
@@ -82,6 +85,8 @@ def test_plan_parity_random():
     ((1, 4, 2, 64), (10, 0, 1, float("nan")), sk.SK_E_ARG),
     ((1, 4, 2, 64), (1000, 0, 1, 0.2), sk.SK_E_BUDGET),
     ((1, 4, 2, 64), (256, 4, 0, 0.5), sk.SK_E_BUDGET),
+    ((1, 4, 2, 64), (10, 0, 1, 0.5, 3), sk.SK_E_ARG),
+    ((1, 4, 2, 64), (100, 30, 1, 0.2, 1), sk.SK_E_BUDGET),     # drop mode: sinks overrun
 ])
 def test_plan_failures(shape, policy, status):
     with pytest.raises(sk.SkError) as e:
@@ -154,6 +159,11 @@ def test_call_validation_without_device():
     assert lib.sk_score_kvnorm(B(shape), 10, FAKE, FAKE, 2, None) == sk.SK_E_ARG
     assert lib.sk_score_kvnorm(B(bad_shape), 10, FAKE, FAKE, 0, None) == sk.SK_E_UNSUPPORTED
     assert lib.sk_score_kvnorm(B(shape), 0, None, None, 0, None) == sk.SK_OK
+    # balanced keys
+    assert lib.sk_balanced_keys(10, 2, None, None) == sk.SK_E_ARG
+    assert lib.sk_balanced_keys(10, -2, FAKE, None) == sk.SK_E_ARG
+    assert lib.sk_balanced_keys((1 << 24) + 5, 4, FAKE, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_balanced_keys(0, 0, None, None) == sk.SK_OK
     # upgrade: sizes, NULLs, alignment, paged argument rules
     assert lib.sk_upgrade_bytes(B(shape), 3) == 2 * 3 * 2 * 2 * 2 * 64
     assert lib.sk_upgrade_bytes(B(shape), -1) == 0
