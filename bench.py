@@ -193,6 +193,33 @@ def main():
                                                        block_table, bs), reps) * 1e-3
     up_bytes = 2 * up_payload.numel() + 4 * n_up                 # rows read + written, list
 
+    # decode attention straight from the payload, all layers in one launch
+    # (one decode query per layer), and the same kernel over an all-fp16
+    # payload of the same request: the bytes a dense-KV attention reads
+    qdec = torch.from_numpy((np.random.default_rng(2).standard_normal((L, Hq, d)) * 0.5)
+                            .astype(np.float16)).to(dev)
+    odec = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
+    ldec = torch.empty((L, Hq), dtype=torch.float32, device=dev)
+    dws = torch.empty(max(1, sk.decode_workspace_bytes(shape, plan, L)), dtype=torch.uint8,
+                      device=dev)
+    t_dec = timed(lambda: sk.decode_attention(shape, plan, payload, qdec, odec, ldec, ws=dws),
+                  reps) * 1e-3
+    pol16 = sk.Policy(n, cfg.sinks, cfg.three_tier, 1.0)
+    plan16 = sk.plan_make(shape, pol16)
+    amap16 = torch.empty_like(amap)
+    order16 = torch.empty_like(order)
+    sk.assign_tiers(pol16, plan16, score, amap16, order16)
+    payload16 = torch.empty(plan16.payload_bytes, dtype=torch.uint8, device=dev)
+    sk.pack(shape, plan16, K, V, amap16, order16, payload16)
+    dws16 = torch.empty(max(1, sk.decode_workspace_bytes(shape, plan16, L)), dtype=torch.uint8,
+                        device=dev)
+    t_dec16 = timed(lambda: sk.decode_attention(shape, plan16, payload16, qdec, odec, ldec,
+                                                ws=dws16), reps) * 1e-3
+    del payload16
+    dec_io = L * Hq * d * (2 + 4) + L * Hq * 4                    # q in, out and lse written
+    dec_bytes = plan.payload_bytes + dec_io
+    dec16_bytes = plan16.payload_bytes + dec_io
+
     # per stage: [steps][launches] durations in ms
     t = {s: np.array([[e[s][2 * j].elapsed_time(e[s][2 * j + 1]) for j in range(len(e[s]) // 2)]
                       for e in all_ev]) for s in stages}
@@ -262,6 +289,12 @@ def main():
                     "pack": rl(up_bytes, t_up_pack, f"upgrade_pack_kernel<{d},{nb}>"),
                     "unpack_paged": rl(up_bytes, t_up_paged,
                                        f"upgrade_unpack_kernel<{d},{nb},true>")},
+        "decode": {"layers": L,
+                   "payload": rl(dec_bytes, t_dec, f"decode_partial_kernel<{d},1,{_pow2(Hq // Hkv)}>"),
+                   "fp16_payload": rl(dec16_bytes, t_dec16,
+                                      f"decode_partial_kernel<{d},0,{_pow2(Hq // Hkv)}>"),
+                   "ms": round(t_dec * 1e3, 4), "fp16_ms": round(t_dec16 * 1e3, 4),
+                   "speedup_vs_fp16": round(t_dec16 / t_dec, 3)},
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "copy_bytes": int(src.numel()),
         "wall_s_timed": round(wall, 3),
@@ -269,6 +302,13 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def _pow2(x):
+    p = 1
+    while p < x:
+        p *= 2
+    return p
 
 
 def score_kernel_names(Hq, Hkv, d):

@@ -13,6 +13,7 @@
  *                                    tier costs
  *   - dequantize (dense or paged) : §4.2 (decode-side dequantization only)
  *   - cold-tier upgrade           : §4.2 and §8 (cold-tier fetch design)
+ *   - decode attention            : §4.2, from the payload without unpacking
  *
  * Conventions shared by every entry point
  *   - Ownership: the caller allocates and frees every buffer.  The library
@@ -306,6 +307,33 @@ sk_status sk_upgrade_pack(const sk_shape* shape, int64_t n_tokens, const void* k
 sk_status sk_upgrade_unpack(const sk_shape* shape, int64_t n_tokens, const void* payload,
                             const uint32_t* tokens, int64_t n_up, void* k_out, void* v_out,
                             const sk_paged* paged, void* stream);
+
+/* --------------------------------------------------------------- decode --
+ * Decode attention straight from the payload (§4.2: the decode worker
+ * dequantizes and runs attention; here the dequantization happens while the
+ * payload is read, with no dense KV).  For every layer l in
+ * [layer0, layer0 + n_layers_q) and query head h (KV head g = h / (H_q/H_kv)):
+ *   o[l][h]   = sum_j softmax_j(q[l][h] . k_hat_j / sqrt(d)) v_hat_j
+ *   lse[l][h] = ln sum_j exp(q[l][h] . k_hat_j / sqrt(d))
+ * over the tokens that were sent (dropped tokens take no part; no causal
+ * mask: a decode query follows the whole prefix), where k_hat, v_hat are
+ * exactly the fp16 rows sk_unpack would write.  The decode step's own new
+ * token is not included: merge it with the returned lse.  With no token
+ * sent, o = 0 and lse = -inf.
+ *   q       : fp16 [n_layers_q][n_q_heads][head_dim], 16-byte aligned
+ *   out     : fp32 [n_layers_q][n_q_heads][head_dim]
+ *   lse     : fp32 [n_layers_q][n_q_heads] (natural log) or NULL
+ *   payload : as written by sk_pack for `plan` (256-byte aligned)
+ *   ws      : at least sk_decode_workspace_bytes(shape, plan, n_layers_q)
+ * Arithmetic: q.k and p.v in fp32 from packed fp16 products; probabilities
+ * are rounded to fp16 once (used in both the numerator and the
+ * denominator), so o is a convex combination of the v_hat rows within
+ * about 1e-3 * max|v_hat| of the exact value.  Deterministic. */
+size_t    sk_decode_workspace_bytes(const sk_shape* shape, const sk_plan* plan,
+                                    int32_t n_layers_q);
+sk_status sk_decode_attention(const sk_shape* shape, const sk_plan* plan, const void* payload,
+                              int32_t layer0, int32_t n_layers_q, const void* q, float* out,
+                              float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ messages -- */
 const char* sk_status_string(sk_status status);

@@ -8,7 +8,8 @@ Python binding; PyTorch only provides device memory and streams.
 
 from .sk import (  # noqa: F401
     OVERFLOW_DROP, OVERFLOW_FALLBACK, OVERFLOW_REJECT, TIER_DROP, Plan, Policy, Shape,
-    SkError, assign_tiers, balanced_keys, colsum_workspace_bytes, lib, pack,
+    SkError, assign_tiers, balanced_keys, colsum_workspace_bytes, decode_attention,
+    decode_workspace_bytes, lib, pack,
     plan_make, recency_weight, score, score_colsum, score_kvnorm, score_rowlse,
     score_workspace_bytes, unpack, unpack_paged, upgrade_bytes, upgrade_pack, upgrade_unpack,
     upgrade_unpack_paged,

@@ -19,7 +19,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsk.so")
 ARCH = "gfx950"
 
-SOURCES = ["sk_api.cpp", "pack.hip", "select.hip", "score.hip", "importance.hip"]
+SOURCES = ["sk_api.cpp", "pack.hip", "select.hip", "score.hip", "importance.hip", "decode.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

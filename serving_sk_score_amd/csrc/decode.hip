@@ -1,0 +1,475 @@
+// Decode attention straight from the mixed-precision payload: the decode
+// worker's attention over the transferred prefix (SpectrumKV paper, §4.2)
+// without the dense unpack.  Every K/V element is dequantized while it is
+// loaded, to exactly the fp16 value the unpack would write
+// (fp16_rne(code * scale)), and the per-tier partial results are merged by
+// their log-sum-exps (the Minima-KV page's per-format partial states are the
+// prior art for that merge).
+//
+// The work is bound by reading the payload (about half the fp16 bytes at
+// b = 0.5).  Per element the vector ALUs only dequantize: fp16 bit patterns
+// 1024 + u are built with v_perm_b32 (u = code + 128 for int8, code + 8 for
+// int4), the bias is removed with one packed fp16 add and the scale applied
+// with one packed fp16 multiply (exact integers, one correctly rounded
+// product).  The contractions go elsewhere:
+//   - q.k runs on the matrix cores: S^T = K Q^T with v_mfma_f32_32x32x16_f16,
+//     32 tokens per row block and the query group's G = H_q/H_kv heads as
+//     columns (held in VGPRs for the whole wavefront; the other 32 - G
+//     columns are zero).  Lane l loads token l%32 of a block and half l/32
+//     of the head dimension, which is exactly the A operand layout when the
+//     contraction runs over the dims of each half in turn.
+//   - p.V runs on the vector ALUs with v_dot2_f32_f16 on (two tokens' values
+//     of one channel, their probabilities rounded to fp16); the dequantized
+//     V rows go through LDS so that lanes can own channel pairs.
+// Softmax is online per head across the chunk's 64-token tiles, base 2
+// (c2 = log2(e)/sqrt(d)); a lane of the S^T fragment owns one head, so the
+// running max and sum stay in registers and only the rescale factor is
+// broadcast.  One wavefront per (layer, KV head, tier, chunk of 64*T slots)
+// writes (m, l, o[d]) per query head; merge_kernel combines the chunks of
+// every tier of a (layer, head) in a fixed order.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "sk_kernels.h"
+
+namespace sk {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <int S>
+__device__ __forceinline__ uint32_t swz_xor_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (S << 10));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// Four int8 codes -> two dwords of fp16 pairs fp16_rne(code * s).
+__device__ __forceinline__ void deq8(uint32_t w, h2 s, uint32_t& lo, uint32_t& hi) {
+    const uint32_t u = w ^ 0x80808080u;  // code + 128 per byte
+    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const h2 a = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + bias;
+    const h2 b = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + bias;
+    lo = as_u32(a * s);
+    hi = as_u32(b * s);
+}
+
+// Eight int4 codes (element 2m in the low nibble of byte m) -> four dwords
+// of fp16 pairs.
+__device__ __forceinline__ void deq4(uint32_t w, h2 s, uint32_t (&o)[4]) {
+    const uint32_t u = w ^ 0x88888888u;           // code + 8 per nibble
+    const uint32_t x = u & 0x0F0F0F0Fu;           // elements 0, 2, 4, 6
+    const uint32_t y = (u >> 4) & 0x0F0F0F0Fu;    // elements 1, 3, 5, 7
+    const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const uint32_t sel[4] = {0x0C040C00u, 0x0C050C01u, 0x0C060C02u, 0x0C070C03u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const h2 a = as_h2(__builtin_amdgcn_perm(y, x, sel[k]) | 0x64006400u) + bias;
+        o[k] = as_u32(a * s);
+    }
+}
+
+constexpr int kPart = 8;  // 16-byte pieces of a row loaded together
+
+// Row bytes per tier and the number of fp16 pairs one 16-byte piece yields.
+template <int D, int TIER>
+struct Tier {
+    static constexpr int RB = TIER == 0 ? 2 * D : (TIER == 1 ? D : D / 2);
+    static constexpr int NP = RB / 16;                          // pieces per row
+    static constexpr int PPP = TIER == 0 ? 4 : (TIER == 1 ? 8 : 16);  // pairs per piece
+};
+
+template <int D, int TIER>
+__device__ __forceinline__ void piece_pairs(u32x4 r, h2 s, uint32_t (&pr)[Tier<D, TIER>::PPP]) {
+    if constexpr (TIER == 0) {
+        pr[0] = r.x;
+        pr[1] = r.y;
+        pr[2] = r.z;
+        pr[3] = r.w;
+    } else if constexpr (TIER == 1) {
+        deq8(r.x, s, pr[0], pr[1]);
+        deq8(r.y, s, pr[2], pr[3]);
+        deq8(r.z, s, pr[4], pr[5]);
+        deq8(r.w, s, pr[6], pr[7]);
+    } else {
+        uint32_t t[4];
+        deq4(r.x, s, t);
+        pr[0] = t[0]; pr[1] = t[1]; pr[2] = t[2]; pr[3] = t[3];
+        deq4(r.y, s, t);
+        pr[4] = t[0]; pr[5] = t[1]; pr[6] = t[2]; pr[7] = t[3];
+        deq4(r.z, s, t);
+        pr[8] = t[0]; pr[9] = t[1]; pr[10] = t[2]; pr[11] = t[3];
+        deq4(r.w, s, t);
+        pr[12] = t[0]; pr[13] = t[1]; pr[14] = t[2]; pr[15] = t[3];
+    }
+}
+
+struct PartialArgs {
+    const uint8_t* payload;
+    int64_t off_code, off_scale;  // this tier's segments
+    int64_t N;                    // tokens in this tier
+    int H, G, Hq;
+    int layer0;
+    const uint16_t* q;            // [nl][Hq][D]
+    float* part;                  // [nl][Hq][NC][D + 2]
+    int64_t chunk_base;           // first global chunk index of this tier
+    int64_t NC;                   // chunks over all tiers
+    int T;                        // 64-token tiles per chunk
+    float c2;                     // log2(e) / sqrt(D)
+};
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ h8 pairs_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    u32x4 v = {a, b, c, d};
+    return __builtin_bit_cast(h8, v);
+}
+
+template <int D, int TIER, int GM>
+__global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
+    using TI = Tier<D, TIER>;
+    constexpr int CP = D / 2;                     // fp16 pairs per row
+    constexpr int HP = CP / 2;                    // pairs per half row
+    constexpr int NPH = TI::NP / 2;               // 16-byte pieces per half row
+    constexpr int KK = D / 16;                    // MFMAs per 32-token block
+    constexpr int LPT = CP < 64 ? CP : 64;        // lanes per token group in p.V
+    constexpr int TG = 64 / LPT;                  // token groups (2 for d = 64)
+    constexpr int DWL = CP / LPT;                 // pairs owned per lane in p.V
+    constexpr int PITCH = CP + 4;                 // LDS row pitch in dwords
+    static_assert(GM <= 32, "query group wider than the MFMA tile");
+    __shared__ uint32_t vt[64 * PITCH];
+    __shared__ uint32_t pp[GM * 32];
+
+    const int lane = threadIdx.x;
+    const int r = lane & 31;   // token within a 32-token block; head column of S^T
+    const int hb = lane >> 5;  // half of the head dimension
+    const int64_t chunk = blockIdx.x;
+    const int g = blockIdx.y;
+    const int li = blockIdx.z;
+    const int64_t layer = a.layer0 + li;
+    const int G = a.G;
+
+    // Q^T as the B operand: column r = head g*G + r (zero past G), rows = the
+    // dims of half hb, 8 per MFMA
+    h8 qb[KK];
+    {
+        const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q) +
+                               ((int64_t)li * a.Hq + (int64_t)g * G + (r < G ? r : 0)) * CP +
+                               hb * HP;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 4 * kk);
+            if (r >= G) v = u32x4{0u, 0u, 0u, 0u};
+            qb[kk] = __builtin_bit_cast(h8, v);
+        }
+    }
+
+    float m = -INFINITY, lsum = 0.0f;  // of head column r
+    float o[GM][DWL][2];
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+        for (int k = 0; k < DWL; ++k) o[h][k][0] = o[h][k][1] = 0.0f;
+
+    for (int tile = 0; tile < a.T; ++tile) {
+        const int64_t s0 = (chunk * a.T + tile) * 64;
+        if (s0 >= a.N) break;
+        f16v c[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int64_t slot = s0 + 32 * blk + r;
+            const bool valid = slot < a.N;
+            const int64_t sl = valid ? slot : a.N - 1;
+            const int64_t rowK = ((layer * a.N + sl) * 2) * a.H + g;
+            const int64_t rowV = rowK + a.H;
+            const uint8_t* kp = a.payload + a.off_code + rowK * TI::RB + hb * (TI::RB / 2);
+            const uint8_t* vp = a.payload + a.off_code + rowV * TI::RB + hb * (TI::RB / 2);
+            h2 sk2 = {(_Float16)1.0f, (_Float16)1.0f}, sv2 = sk2;
+            if constexpr (TIER != 0) {
+                const uint16_t* sc = reinterpret_cast<const uint16_t*>(a.payload + a.off_scale);
+                const _Float16 skh = __builtin_bit_cast(_Float16, sc[rowK]);
+                const _Float16 svh = __builtin_bit_cast(_Float16, sc[rowV]);
+                sk2 = h2{skh, skh};
+                sv2 = h2{svh, svh};
+            }
+            u32x4 kr[NPH], vr[NPH];
+#pragma unroll
+            for (int i = 0; i < NPH; ++i) {
+                kr[i] = ld16(kp + i * 16);
+                vr[i] = ld16(vp + i * 16);
+            }
+            uint32_t kpairs[HP];
+#pragma unroll
+            for (int i = 0; i < NPH; ++i) {
+                uint32_t pr[TI::PPP];
+                piece_pairs<D, TIER>(kr[i], sk2, pr);
+#pragma unroll
+                for (int e = 0; e < TI::PPP; ++e) kpairs[i * TI::PPP + e] = pr[e];
+            }
+            c[blk] = f16v{};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                c[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    pairs_h8(kpairs[4 * kk], kpairs[4 * kk + 1], kpairs[4 * kk + 2],
+                             kpairs[4 * kk + 3]),
+                    qb[kk], c[blk], 0, 0, 0);
+            uint32_t* vrow = &vt[(32 * blk + r) * PITCH + hb * HP];
+#pragma unroll
+            for (int i = 0; i < NPH; ++i) {
+                uint32_t pv[TI::PPP];
+                piece_pairs<D, TIER>(vr[i], sv2, pv);
+#pragma unroll
+                for (int e = 0; e < TI::PPP; e += 4) {
+                    u32x4 w;
+                    w.x = valid ? pv[e] : 0u;
+                    w.y = valid ? pv[e + 1] : 0u;
+                    w.z = valid ? pv[e + 2] : 0u;
+                    w.w = valid ? pv[e + 3] : 0u;
+                    *reinterpret_cast<u32x4*>(vrow + i * TI::PPP + e) = w;
+                }
+            }
+        }
+
+        // S^T fragment: lane holds head r, tokens 32*blk + 8*(e/4) + 4*hb + e%4
+        float sv[2][16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t tok = s0 + 32 * blk + 8 * (e / 4) + 4 * hb + (e % 4);
+                const float s = tok < a.N ? c[blk][e] * a.c2 : -INFINITY;
+                sv[blk][e] = s;
+                mx = fmaxf(mx, s);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile
+        m = mn;
+        float ps = 0.0f;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) {
+                const _Float16 p0 = (_Float16)__builtin_amdgcn_exp2f(sv[blk][e] - mn);
+                const _Float16 p1 = (_Float16)__builtin_amdgcn_exp2f(sv[blk][e + 1] - mn);
+                const _Float16 p2 = (_Float16)__builtin_amdgcn_exp2f(sv[blk][e + 2] - mn);
+                const _Float16 p3 = (_Float16)__builtin_amdgcn_exp2f(sv[blk][e + 3] - mn);
+                ps += ((float)p0 + (float)p1) + ((float)p2 + (float)p3);
+                if (r < GM) {
+                    // token pair index (32*blk + 8*(e/4) + 4*hb) / 2 and the next one
+                    const int pi = 16 * blk + 4 * (e / 4) + 2 * hb;
+                    uint2 w;
+                    w.x = as_u32(h2{p0, p1});
+                    w.y = as_u32(h2{p2, p3});
+                    *reinterpret_cast<uint2*>(&pp[r * 32 + pi]) = w;
+                }
+            }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            const float al = __shfl(alpha, h, 64);
+#pragma unroll
+            for (int k = 0; k < DWL; ++k) {
+                o[h][k][0] *= al;
+                o[h][k][1] *= al;
+            }
+        }
+        __syncthreads();
+
+        // p.V: lanes own channel pairs, tokens two at a time
+        const int tg = lane / LPT;
+        const int wl = lane % LPT;
+#pragma unroll 4
+        for (int tp = tg; tp < 32; tp += TG) {
+#pragma unroll
+            for (int k = 0; k < DWL; ++k) {
+                const int w = wl + k * LPT;
+                const uint32_t x = vt[(2 * tp) * PITCH + w];
+                const uint32_t y = vt[(2 * tp + 1) * PITCH + w];
+                const h2 a0 = as_h2(__builtin_amdgcn_perm(y, x, 0x05040100u));
+                const h2 a1 = as_h2(__builtin_amdgcn_perm(y, x, 0x07060302u));
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+                    const h2 pw = as_h2(pp[h * 32 + tp]);
+                    o[h][k][0] = __builtin_amdgcn_fdot2(a0, pw, o[h][k][0], false);
+                    o[h][k][1] = __builtin_amdgcn_fdot2(a1, pw, o[h][k][1], false);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // lanes r and r + 32 hold the same head's two token halves
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    float* recs = a.part + (((int64_t)li * a.Hq + (int64_t)g * G) * a.NC + a.chunk_base + chunk) *
+                               (D + 2);
+    const int64_t hstride = a.NC * (D + 2);  // between consecutive heads
+    if (lane < G) {
+        recs[lane * hstride] = m;
+        recs[lane * hstride + 1] = ltot;
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+        if constexpr (TG > 1) {
+#pragma unroll
+            for (int k = 0; k < DWL; ++k) {
+                o[h][k][0] += __shfl_xor(o[h][k][0], 32, 64);
+                o[h][k][1] += __shfl_xor(o[h][k][1], 32, 64);
+            }
+        }
+        if (h >= G) continue;
+        if (lane < LPT) {
+            float* rec = recs + h * hstride;
+#pragma unroll
+            for (int k = 0; k < DWL; ++k) {
+                const int w = lane + k * LPT;
+                rec[2 + 2 * w] = o[h][k][0];
+                rec[2 + 2 * w + 1] = o[h][k][1];
+            }
+        }
+    }
+}
+
+// One wavefront per (layer, query head): chunks combined in index order.
+template <int D>
+__global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ part, int64_t NC,
+                                                   int Hq, float* __restrict__ out,
+                                                   float* __restrict__ lse) {
+    constexpr int CPL = (D + 63) / 64;  // channels per lane
+    const int lane = threadIdx.x;
+    const int h = blockIdx.x;
+    const int li = blockIdx.y;
+    const float* rec0 = part + ((int64_t)li * Hq + h) * NC * (D + 2);
+    float M = -INFINITY;
+    for (int64_t c = lane; c < NC; c += 64) M = fmaxf(M, rec0[c * (D + 2)]);
+    M = wave_max(M);
+    float L = 0.0f, acc[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[k] = 0.0f;
+    if (M != -INFINITY) {
+        for (int64_t c = 0; c < NC; ++c) {
+            const float* rec = rec0 + c * (D + 2);
+            const float w = __builtin_amdgcn_exp2f(rec[0] - M);  // 0 for an empty chunk
+            L += w * rec[1];
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                const int ch = lane + 64 * k;
+                if (ch < D) acc[k] += w * rec[2 + ch];
+            }
+        }
+    }
+    float* o = out + ((int64_t)li * Hq + h) * D;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const int ch = lane + 64 * k;
+        if (ch < D) o[ch] = L > 0.0f ? acc[k] / L : 0.0f;
+    }
+    if (lse && lane == 0)
+        lse[(int64_t)li * Hq + h] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+template <int D, int TIER>
+hipError_t launch_tier(const PartialArgs& a, int nl, int GM, hipStream_t st) {
+    const dim3 grid((unsigned)((a.N + 64 * (int64_t)a.T - 1) / (64 * (int64_t)a.T)), (unsigned)a.H,
+                    (unsigned)nl);
+    switch (GM) {
+        case 1: decode_partial_kernel<D, TIER, 1><<<grid, 64, 0, st>>>(a); break;
+        case 2: decode_partial_kernel<D, TIER, 2><<<grid, 64, 0, st>>>(a); break;
+        case 4: decode_partial_kernel<D, TIER, 4><<<grid, 64, 0, st>>>(a); break;
+        case 8: decode_partial_kernel<D, TIER, 8><<<grid, 64, 0, st>>>(a); break;
+        default: decode_partial_kernel<D, TIER, 16><<<grid, 64, 0, st>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_all(const PartialArgs& base, const TierSeg seg[3], int nl, int GM, float* out,
+                      float* lse, hipStream_t st) {
+    PartialArgs a = base;
+    int64_t cb = 0;
+    for (int t = 0; t < 3; ++t) {
+        const int64_t N = seg[t].count;
+        if (N == 0) continue;
+        a.off_code = seg[t].off_code;
+        a.off_scale = seg[t].off_scale;
+        a.N = N;
+        a.chunk_base = cb;
+        hipError_t e = t == 0 ? launch_tier<D, 0>(a, nl, GM, st)
+                              : (t == 1 ? launch_tier<D, 1>(a, nl, GM, st)
+                                        : launch_tier<D, 2>(a, nl, GM, st));
+        if (e != hipSuccess) return e;
+        cb += (N + 64 * (int64_t)a.T - 1) / (64 * (int64_t)a.T);
+    }
+    merge_kernel<D><<<dim3((unsigned)base.Hq, (unsigned)nl), 64, 0, st>>>(base.part, base.NC,
+                                                                          base.Hq, out, lse);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_tiles_per_chunk(const Dims& s, const TierSeg seg[3], int nl) {
+    int64_t tiles = 0;
+    for (int t = 0; t < 3; ++t) tiles += (seg[t].count + 63) / 64;
+    tiles *= (int64_t)s.Hkv * nl;
+    int T = 1;
+    while (T < 8 && tiles / (2 * T) >= 4096) T *= 2;  // keep >= 4096 wavefronts
+    return T;
+}
+
+int64_t decode_chunks(const Dims& s, const TierSeg seg[3], int nl) {
+    const int64_t span = 64 * (int64_t)decode_tiles_per_chunk(s, seg, nl);
+    int64_t nc = 0;
+    for (int t = 0; t < 3; ++t) nc += (seg[t].count + span - 1) / span;
+    return nc;
+}
+
+hipError_t launch_decode(const Dims& s, const TierSeg seg[3], const void* payload, int layer0,
+                         int nl, const void* q, float* out, float* lse, float* part,
+                         hipStream_t st) {
+    PartialArgs a;
+    a.payload = static_cast<const uint8_t*>(payload);
+    a.off_code = a.off_scale = 0;
+    a.N = 0;
+    a.H = s.Hkv;
+    a.G = s.Hq / s.Hkv;
+    a.Hq = s.Hq;
+    a.layer0 = layer0;
+    a.q = static_cast<const uint16_t*>(q);
+    a.part = part;
+    a.chunk_base = 0;
+    a.NC = decode_chunks(s, seg, nl);
+    a.T = decode_tiles_per_chunk(s, seg, nl);
+    a.c2 = 1.4426950408889634f / sqrtf((float)s.d);
+    int GM = 1;
+    while (GM < a.G) GM *= 2;
+    switch (s.d) {
+        case 64: return launch_all<64>(a, seg, nl, GM, out, lse, st);
+        case 128: return launch_all<128>(a, seg, nl, GM, out, lse, st);
+        case 256: return launch_all<256>(a, seg, nl, GM, out, lse, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sk

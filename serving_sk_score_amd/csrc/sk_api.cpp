@@ -399,6 +399,45 @@ sk_status sk_unpack(const sk_shape* shape, const sk_plan* plan, const void* payl
                   "unpack");
 }
 
+static size_t decode_ws(const sk_shape* shape, const sk_plan* plan, int32_t nl) {
+    sk::TierSeg seg[3];
+    segs(plan, seg);
+    return align256((size_t)nl * (size_t)shape->n_q_heads *
+                    (size_t)sk::decode_chunks(dims(shape, plan->n_tokens), seg, nl) *
+                    (size_t)(shape->head_dim + 2) * sizeof(float));
+}
+
+size_t sk_decode_workspace_bytes(const sk_shape* shape, const sk_plan* plan, int32_t nl) {
+    if (check_shape(shape) || check_plan(plan, shape) || nl < 1 || nl > shape->n_layers) return 0;
+    return decode_ws(shape, plan, nl);
+}
+
+sk_status sk_decode_attention(const sk_shape* shape, const sk_plan* plan, const void* payload,
+                              int32_t layer0, int32_t nl, const void* q, float* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+    if (sk_status st = check_shape(shape)) return st;
+    if (sk_status st = check_plan(plan, shape)) return st;
+    if (nl < 1 || layer0 < 0 || (int64_t)layer0 + nl > shape->n_layers)
+        return fail(SK_E_ARG, "layers [%d, %d + %d) outside [0, %d)", layer0, layer0, nl,
+                    shape->n_layers);
+    if (!q || !out) return fail(SK_E_ARG, "q and out must be non-NULL");
+    if (!aligned(q, 16)) return fail(SK_E_ARG, "q must be 16-byte aligned");
+    if (!aligned(out, 4) || !aligned(lse, 4)) return fail(SK_E_ARG, "out and lse must be 4-byte aligned");
+    const bool sent = plan->n16 + plan->n8 + plan->n4 > 0;
+    if (sent && !payload) return fail(SK_E_ARG, "payload must be non-NULL");
+    if (!aligned(payload, 256)) return fail(SK_E_ARG, "payload must be 256-byte aligned");
+    const size_t need = decode_ws(shape, plan, nl);
+    if (need && (!ws || ws_bytes < need))
+        return fail(SK_E_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");
+    sk::TierSeg seg[3];
+    segs(plan, seg);
+    (void)hipGetLastError();
+    return device(sk::launch_decode(dims(shape, plan->n_tokens), seg, payload, layer0, nl, q, out,
+                                    lse, (float*)ws, (hipStream_t)stream),
+                  "decode attention");
+}
+
 size_t sk_upgrade_bytes(const sk_shape* shape, int64_t m) {
     if (check_shape(shape) || m < 0 || m >= kMaxTokens) return 0;
     return (size_t)shape->n_layers * (size_t)m * 2 * (size_t)shape->n_kv_heads * 2 *

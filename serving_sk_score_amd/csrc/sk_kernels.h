@@ -60,6 +60,14 @@ hipError_t launch_upgrade_unpack(const Dims& s, int64_t m, const void* payload,
                                  const int32_t* block_table, int32_t block_size,
                                  int64_t num_blocks, hipStream_t st);
 
+// decode attention from the payload: partial records fp32
+// [nl][Hq][decode_chunks][d + 2], then out fp32 [nl][Hq][d] and lse fp32 [nl][Hq]
+int decode_tiles_per_chunk(const Dims& s, const TierSeg seg[3], int nl);
+int64_t decode_chunks(const Dims& s, const TierSeg seg[3], int nl);
+hipError_t launch_decode(const Dims& s, const TierSeg seg[3], const void* payload, int layer0,
+                         int nl, const void* q, float* out, float* lse, float* part,
+                         hipStream_t st);
+
 // score variants: KV-norm fallback (score fp32 [n]) and recency weighting
 hipError_t launch_kvnorm(const Dims& s, const void* k, float* score, int accumulate,
                          hipStream_t st);

@@ -25,7 +25,8 @@ EXPORTS = [
     "sk_score_colsum_workspace_bytes", "sk_score_colsum", "sk_assign_workspace_bytes",
     "sk_assign_tiers", "sk_pack", "sk_unpack", "sk_status_string", "sk_last_error",
     "sk_layout_version", "sk_recency_weight", "sk_score_kvnorm", "sk_upgrade_bytes",
-    "sk_upgrade_pack", "sk_upgrade_unpack", "sk_balanced_keys",
+    "sk_upgrade_pack", "sk_upgrade_unpack", "sk_balanced_keys", "sk_decode_workspace_bytes",
+    "sk_decode_attention",
 ]
 
 
@@ -119,6 +120,9 @@ def lib():
             "sk_score_kvnorm": (i32, [P(_Shape), i64, vp, vp, i32, vp]),
             "sk_upgrade_bytes": (sz, [P(_Shape), i64]),
             "sk_balanced_keys": (i32, [i64, i32, vp, vp]),
+            "sk_decode_workspace_bytes": (sz, [P(_Shape), P(_Plan), i32]),
+            "sk_decode_attention": (i32, [P(_Shape), P(_Plan), vp, i32, i32, vp, vp, vp, vp, sz,
+                                          vp]),
             "sk_upgrade_pack": (i32, [P(_Shape), i64, vp, vp, vp, i64, vp, vp]),
             "sk_upgrade_unpack": (i32, [P(_Shape), i64, vp, vp, i64, vp, vp, P(_Paged), vp]),
         }
@@ -363,3 +367,28 @@ def upgrade_unpack_paged(shape: Shape, n: int, payload, tokens, k_cache, v_cache
     _check(lib().sk_upgrade_unpack(ctypes.byref(shape.c()), n, _ptr(payload), _ptr(tokens), m,
                                    None, None, ctypes.byref(pg), _stream(payload)))
     return k_cache, v_cache
+
+
+def decode_workspace_bytes(shape: Shape, plan: Plan, n_layers_q: int) -> int:
+    return int(lib().sk_decode_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(plan.c),
+                                               n_layers_q))
+
+
+def decode_attention(shape: Shape, plan: Plan, payload, q, out, lse=None, layer0=0, ws=None):
+    """Attention of q (fp16 [nl][H_q][d], layers layer0..layer0+nl-1) over the
+    sent tokens, read straight from the payload; out fp32 [nl][H_q][d], lse
+    fp32 [nl][H_q] (natural log) or None."""
+    nl = q.shape[0] if q.dim() == 3 else -1
+    _need(q, "q", torch.float16, shape=(nl, shape.n_q_heads, shape.head_dim))
+    _need(out, "out", torch.float32, shape=(nl, shape.n_q_heads, shape.head_dim))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(nl, shape.n_q_heads))
+    _need(payload, "payload", torch.uint8, numel=plan.payload_bytes)
+    need = decode_workspace_bytes(shape, plan, nl)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(ws, "ws", torch.uint8, numel=need)
+    _check(lib().sk_decode_attention(ctypes.byref(shape.c()), ctypes.byref(plan.c), _ptr(payload),
+                                     layer0, nl, _ptr(q), _ptr(out), _ptr(lse), _ptr(ws),
+                                     ws.numel(), _stream(q)))
+    return out

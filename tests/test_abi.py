@@ -136,6 +136,16 @@ def test_call_validation_without_device():
     # pack / unpack: corrupted plan, shape mismatch, misaligned payload
     bad = sk._Plan.from_buffer_copy(pc)
     bad.n8 += 1
+    # decode attention: layer range, NULLs, alignment, workspace
+    dws = lib.sk_decode_workspace_bytes(B(shape), B(pc), 2)
+    assert dws > 0 and lib.sk_decode_workspace_bytes(B(shape), B(pc), 3) == 0
+    assert lib.sk_decode_attention(B(shape), B(pc), FAKE, 1, 2, FAKE, FAKE, None, FAKE, dws, None) == sk.SK_E_ARG
+    assert lib.sk_decode_attention(B(shape), B(pc), FAKE, 0, 0, FAKE, FAKE, None, FAKE, dws, None) == sk.SK_E_ARG
+    assert lib.sk_decode_attention(B(shape), B(pc), FAKE, 0, 2, None, FAKE, None, FAKE, dws, None) == sk.SK_E_ARG
+    assert lib.sk_decode_attention(B(shape), B(pc), FAKE, 0, 2, FAKE_MIS, FAKE, None, FAKE, dws, None) == sk.SK_E_ARG
+    assert lib.sk_decode_attention(B(shape), B(pc), FAKE, 0, 2, FAKE, FAKE, None, FAKE, dws - 1, None) == sk.SK_E_WORKSPACE
+    assert lib.sk_decode_attention(B(shape), B(bad), FAKE, 0, 2, FAKE, FAKE, None, FAKE, dws, None) == sk.SK_E_ARG
+    assert lib.sk_decode_attention(B(shape), B(pc), ctypes.c_void_p(0x7F0000001010), 0, 2, FAKE, FAKE, None, FAKE, dws, None) == sk.SK_E_ARG
     assert lib.sk_pack(B(shape), B(bad), FAKE, FAKE, FAKE, None, FAKE, None) == sk.SK_E_ARG
     shape2, _ = _c((3, 4, 2, 64))
     assert lib.sk_pack(B(shape2), B(pc), FAKE, FAKE, FAKE, None, FAKE, None) == sk.SK_E_ARG
