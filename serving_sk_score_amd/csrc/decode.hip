@@ -32,6 +32,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "sk_kernels.h"
 
 namespace sk {
@@ -43,8 +45,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Cached 16-byte load: one load instruction reads 32 bytes of each of 32
+// rows, so a row's 128-byte line is consumed by consecutive instructions and
+// must stay cached between them.
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return *reinterpret_cast<const u32x4*>(p);
 }
 
 template <int S>
@@ -124,15 +129,20 @@ __device__ __forceinline__ void piece_pairs(u32x4 r, h2 s, uint32_t (&pr)[Tier<D
     }
 }
 
+struct TierArgs {
+    int64_t off_code, off_scale;  // the tier's segments
+    int64_t N;                    // tokens in the tier
+    int64_t chunk_base;           // first global chunk index of the tier
+};
+
 struct PartialArgs {
     const uint8_t* payload;
-    int64_t off_code, off_scale;  // this tier's segments
-    int64_t N;                    // tokens in this tier
+    TierArgs tier[3];
+    int64_t cend[3];              // cumulative chunk counts: tier t owns [cend[t-1], cend[t])
     int H, G, Hq;
     int layer0;
     const uint16_t* q;            // [nl][Hq][D]
     float* part;                  // [nl][Hq][NC][D + 2]
-    int64_t chunk_base;           // first global chunk index of this tier
     int64_t NC;                   // chunks over all tiers
     int T;                        // 64-token tiles per chunk
     float c2;                     // log2(e) / sqrt(D)
@@ -146,8 +156,20 @@ __device__ __forceinline__ h8 pairs_h8(uint32_t a, uint32_t b, uint32_t c, uint3
     return __builtin_bit_cast(h8, v);
 }
 
+// The K and V half rows of one 32-token block as loaded by one lane, with
+// their scales.
+template <int NPH>
+struct BlockRegs {
+    u32x4 k[NPH], v[NPH];
+    uint16_t sk, sv;  // fp16 scale bits
+};
+
+template <int D>
+constexpr int lds_pitch() { return D / 2 + 4; }  // V row pitch in dwords
+
 template <int D, int TIER, int GM>
-__global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
+__device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArgs& ta,
+                                             int64_t chunk, uint32_t* vt, uint32_t* pp) {
     using TI = Tier<D, TIER>;
     constexpr int CP = D / 2;                     // fp16 pairs per row
     constexpr int HP = CP / 2;                    // pairs per half row
@@ -156,19 +178,18 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
     constexpr int LPT = CP < 64 ? CP : 64;        // lanes per token group in p.V
     constexpr int TG = 64 / LPT;                  // token groups (2 for d = 64)
     constexpr int DWL = CP / LPT;                 // pairs owned per lane in p.V
-    constexpr int PITCH = CP + 4;                 // LDS row pitch in dwords
+    constexpr int PITCH = lds_pitch<D>();         // vt: [64 tokens][PITCH] dwords
     static_assert(GM <= 32, "query group wider than the MFMA tile");
-    __shared__ uint32_t vt[64 * PITCH];
-    __shared__ uint32_t pp[GM * 32];
+    // pp: [32 token pairs][GM heads] fp16 probability pairs
 
     const int lane = threadIdx.x;
     const int r = lane & 31;   // token within a 32-token block; head column of S^T
     const int hb = lane >> 5;  // half of the head dimension
-    const int64_t chunk = blockIdx.x;
     const int g = blockIdx.y;
     const int li = blockIdx.z;
     const int64_t layer = a.layer0 + li;
     const int G = a.G;
+    const int64_t N = ta.N;
 
     // Q^T as the B operand: column r = head g*G + r (zero past G), rows = the
     // dims of half hb, 8 per MFMA
@@ -185,105 +206,137 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
         }
     }
 
-    float m = -INFINITY, lsum = 0.0f;  // of head column r
+    const uint8_t* code = a.payload + ta.off_code + hb * (TI::RB / 2);
+    const uint16_t* scale = reinterpret_cast<const uint16_t*>(a.payload + ta.off_scale);
+    // issue the loads of the 32-token block starting at slot b0 (slots past
+    // the tier's end re-load its last token; they are masked later)
+    auto load_block = [&](BlockRegs<NPH>& R, int64_t b0) {
+        const int64_t slot = b0 + r < N ? b0 + r : N - 1;
+        const int64_t rowK = ((layer * N + slot) * 2) * a.H + g;
+        const int64_t rowV = rowK + a.H;
+        const uint8_t* kp = code + rowK * TI::RB;
+        const uint8_t* vp = code + rowV * TI::RB;
+#pragma unroll
+        for (int i = 0; i < NPH; ++i) {
+            R.k[i] = ld16(kp + i * 16);
+            R.v[i] = ld16(vp + i * 16);
+        }
+        if constexpr (TIER != 0) {
+            R.sk = scale[rowK];
+            R.sv = scale[rowV];
+        }
+    };
+    // an ordering point: nothing computed from R may move above it, so the
+    // loads issued just before it are in flight while R is used
+    auto pin = [&](BlockRegs<NPH>& R) {
+#pragma unroll
+        for (int i = 0; i < NPH; ++i) asm volatile("" : "+v"(R.k[i]), "+v"(R.v[i]));
+        if constexpr (TIER != 0) asm volatile("" : "+v"(R.sk), "+v"(R.sv));
+    };
+    // dequantize a block: K into the S^T MFMAs, V into its LDS rows (rows of
+    // slots past the tier's end hold a copy of its last token; their
+    // probabilities are exactly 0)
+    auto process_block = [&](const BlockRegs<NPH>& R, int blk, f16v& c) {
+        h2 sk2 = {(_Float16)1.0f, (_Float16)1.0f}, sv2 = sk2;
+        if constexpr (TIER != 0) {
+            // consumed here, not earlier: a wait for a prefetched block's
+            // scale would also wait for every load issued before it
+            uint32_t ks = R.sk, vs = R.sv;
+            asm volatile("" : "+v"(ks), "+v"(vs));
+            sk2 = as_h2(ks | (ks << 16));
+            sv2 = as_h2(vs | (vs << 16));
+        }
+        uint32_t kpairs[HP];
+#pragma unroll
+        for (int i = 0; i < NPH; ++i) {
+            uint32_t pr[TI::PPP];
+            piece_pairs<D, TIER>(R.k[i], sk2, pr);
+#pragma unroll
+            for (int e = 0; e < TI::PPP; ++e) kpairs[i * TI::PPP + e] = pr[e];
+        }
+        c = f16v{};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                pairs_h8(kpairs[4 * kk], kpairs[4 * kk + 1], kpairs[4 * kk + 2], kpairs[4 * kk + 3]),
+                qb[kk], c, 0, 0, 0);
+        uint32_t* vrow = &vt[(32 * blk + r) * PITCH + hb * HP];
+#pragma unroll
+        for (int i = 0; i < NPH; ++i) {
+            uint32_t pv[TI::PPP];
+            piece_pairs<D, TIER>(R.v[i], sv2, pv);
+#pragma unroll
+            for (int e = 0; e < TI::PPP; e += 4)
+                *reinterpret_cast<u32x4*>(vrow + i * TI::PPP + e) =
+                    u32x4{pv[e], pv[e + 1], pv[e + 2], pv[e + 3]};
+        }
+    };
+
+    float m = -INFINITY, lsum = 0.0f;  // of head column r, scaled (base-2) domain
     float o[GM][DWL][2];
 #pragma unroll
     for (int h = 0; h < GM; ++h)
 #pragma unroll
         for (int k = 0; k < DWL; ++k) o[h][k][0] = o[h][k][1] = 0.0f;
 
-    for (int tile = 0; tile < a.T; ++tile) {
-        const int64_t s0 = (chunk * a.T + tile) * 64;
-        if (s0 >= a.N) break;
+    BlockRegs<NPH> A, B;
+    // one 64-token tile: blocks s0 and s0 + 32 (A holds the first, already
+    // loaded); the next tile's first block is loaded while this one is used
+    // (the prefetch is a compile-time choice: a load issued on one branch only
+    // would make the wait counts of the merged paths conservative)
+    // Holding the next block while using this one doubles the load registers;
+    // measured, it pays even where it leaves one wave per SIMD (8 pieces per
+    // half row: fp16 at d = 128, int8 at d = 256).  fp16 rows at d = 256 (16
+    // pieces) would spill: there both blocks of a tile are loaded at its start.
+    constexpr bool PREF = NPH <= 8;
+    auto tile_body = [&](auto masked, auto prefetch, int64_t s0) {
+        constexpr bool MASKED = decltype(masked)::value;
+        constexpr bool PREFETCH = PREF && decltype(prefetch)::value;
         f16v c[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int64_t slot = s0 + 32 * blk + r;
-            const bool valid = slot < a.N;
-            const int64_t sl = valid ? slot : a.N - 1;
-            const int64_t rowK = ((layer * a.N + sl) * 2) * a.H + g;
-            const int64_t rowV = rowK + a.H;
-            const uint8_t* kp = a.payload + a.off_code + rowK * TI::RB + hb * (TI::RB / 2);
-            const uint8_t* vp = a.payload + a.off_code + rowV * TI::RB + hb * (TI::RB / 2);
-            h2 sk2 = {(_Float16)1.0f, (_Float16)1.0f}, sv2 = sk2;
-            if constexpr (TIER != 0) {
-                const uint16_t* sc = reinterpret_cast<const uint16_t*>(a.payload + a.off_scale);
-                const _Float16 skh = __builtin_bit_cast(_Float16, sc[rowK]);
-                const _Float16 svh = __builtin_bit_cast(_Float16, sc[rowV]);
-                sk2 = h2{skh, skh};
-                sv2 = h2{svh, svh};
-            }
-            u32x4 kr[NPH], vr[NPH];
-#pragma unroll
-            for (int i = 0; i < NPH; ++i) {
-                kr[i] = ld16(kp + i * 16);
-                vr[i] = ld16(vp + i * 16);
-            }
-            uint32_t kpairs[HP];
-#pragma unroll
-            for (int i = 0; i < NPH; ++i) {
-                uint32_t pr[TI::PPP];
-                piece_pairs<D, TIER>(kr[i], sk2, pr);
-#pragma unroll
-                for (int e = 0; e < TI::PPP; ++e) kpairs[i * TI::PPP + e] = pr[e];
-            }
-            c[blk] = f16v{};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                c[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    pairs_h8(kpairs[4 * kk], kpairs[4 * kk + 1], kpairs[4 * kk + 2],
-                             kpairs[4 * kk + 3]),
-                    qb[kk], c[blk], 0, 0, 0);
-            uint32_t* vrow = &vt[(32 * blk + r) * PITCH + hb * HP];
-#pragma unroll
-            for (int i = 0; i < NPH; ++i) {
-                uint32_t pv[TI::PPP];
-                piece_pairs<D, TIER>(vr[i], sv2, pv);
-#pragma unroll
-                for (int e = 0; e < TI::PPP; e += 4) {
-                    u32x4 w;
-                    w.x = valid ? pv[e] : 0u;
-                    w.y = valid ? pv[e + 1] : 0u;
-                    w.z = valid ? pv[e + 2] : 0u;
-                    w.w = valid ? pv[e + 3] : 0u;
-                    *reinterpret_cast<u32x4*>(vrow + i * TI::PPP + e) = w;
-                }
-            }
-        }
+        if constexpr (!PREF) load_block(A, s0);
+        load_block(B, s0 + 32);
+        if constexpr (PREF) pin(A);
+        process_block(A, 0, c[0]);
+        if constexpr (PREFETCH) load_block(A, s0 + 64);
+        if constexpr (PREF) pin(B);
+        process_block(B, 1, c[1]);
 
         // S^T fragment: lane holds head r, tokens 32*blk + 8*(e/4) + 4*hb + e%4
-        float sv[2][16];
+        if constexpr (MASKED) {
+            const int rem = (int)(N - s0);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (32 * blk + 8 * (e / 4) + 4 * hb + (e % 4) >= rem) c[blk][e] = -INFINITY;
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t tok = s0 + 32 * blk + 8 * (e / 4) + 4 * hb + (e % 4);
-                const float s = tok < a.N ? c[blk][e] * a.c2 : -INFINITY;
-                sv[blk][e] = s;
-                mx = fmaxf(mx, s);
-            }
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, c[blk][e]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m, mx);
+        const float mn = fmaxf(m, mx * a.c2);
         const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile
         m = mn;
+        const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
         float ps = 0.0f;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int e = 0; e < 16; e += 4) {
-                const _Float16 p0 = (_Float16)__builtin_amdgcn_exp2f(sv[blk][e] - mn);
-                const _Float16 p1 = (_Float16)__builtin_amdgcn_exp2f(sv[blk][e + 1] - mn);
-                const _Float16 p2 = (_Float16)__builtin_amdgcn_exp2f(sv[blk][e + 2] - mn);
-                const _Float16 p3 = (_Float16)__builtin_amdgcn_exp2f(sv[blk][e + 3] - mn);
-                ps += ((float)p0 + (float)p1) + ((float)p2 + (float)p3);
+                h2 p01, p23;
+                p01.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(c[blk][e], a.c2, -mn));
+                p01.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(c[blk][e + 1], a.c2, -mn));
+                p23.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(c[blk][e + 2], a.c2, -mn));
+                p23.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(c[blk][e + 3], a.c2, -mn));
+                ps = __builtin_amdgcn_fdot2(p01, ones, ps, false);
+                ps = __builtin_amdgcn_fdot2(p23, ones, ps, false);
                 if (r < GM) {
-                    // token pair index (32*blk + 8*(e/4) + 4*hb) / 2 and the next one
+                    // token pairs (32*blk + 8*(e/4) + 4*hb) / 2 and the next one
                     const int pi = 16 * blk + 4 * (e / 4) + 2 * hb;
-                    uint2 w;
-                    w.x = as_u32(h2{p0, p1});
-                    w.y = as_u32(h2{p2, p3});
-                    *reinterpret_cast<uint2*>(&pp[r * 32 + pi]) = w;
+                    pp[pi * GM + r] = as_u32(p01);
+                    pp[(pi + 1) * GM + r] = as_u32(p23);
                 }
             }
         lsum = lsum * alpha + ps;
@@ -299,10 +352,14 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
         __syncthreads();
 
         // p.V: lanes own channel pairs, tokens two at a time
-        const int tg = lane / LPT;
-        const int wl = lane % LPT;
-#pragma unroll 4
-        for (int tp = tg; tp < 32; tp += TG) {
+        const int tg = TG > 1 ? lane / LPT : 0;
+        const int wl = TG > 1 ? lane % LPT : lane;
+#pragma unroll
+        for (int it = 0; it < 32 / TG; ++it) {
+            const int tp = it * TG + tg;
+            uint32_t pw[GM];
+#pragma unroll
+            for (int h = 0; h < GM; ++h) pw[h] = pp[tp * GM + h];
 #pragma unroll
             for (int k = 0; k < DWL; ++k) {
                 const int w = wl + k * LPT;
@@ -312,18 +369,35 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
                 const h2 a1 = as_h2(__builtin_amdgcn_perm(y, x, 0x07060302u));
 #pragma unroll
                 for (int h = 0; h < GM; ++h) {
-                    const h2 pw = as_h2(pp[h * 32 + tp]);
-                    o[h][k][0] = __builtin_amdgcn_fdot2(a0, pw, o[h][k][0], false);
-                    o[h][k][1] = __builtin_amdgcn_fdot2(a1, pw, o[h][k][1], false);
+                    o[h][k][0] = __builtin_amdgcn_fdot2(a0, as_h2(pw[h]), o[h][k][0], false);
+                    o[h][k][1] = __builtin_amdgcn_fdot2(a1, as_h2(pw[h]), o[h][k][1], false);
                 }
             }
         }
         __syncthreads();
+    };
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    const int64_t c0 = chunk * a.T * 64;
+    const int64_t c1 = c0 + a.T * 64 < N ? c0 + a.T * 64 : N;  // end of this chunk
+    const int64_t nfull = (c1 - c0) / 64;                       // whole tiles
+    const bool tail = c0 + nfull * 64 < c1;
+    if constexpr (PREF) load_block(A, c0);
+    int64_t s0 = c0;
+    for (int64_t t = 0; t + 1 < nfull; ++t, s0 += 64) tile_body(no{}, yes{}, s0);
+    if (nfull > 0) {
+        if (tail)
+            tile_body(no{}, yes{}, s0);
+        else
+            tile_body(no{}, no{}, s0);
+        s0 += 64;
     }
+    if (tail) tile_body(yes{}, no{}, s0);
 
     // lanes r and r + 32 hold the same head's two token halves
     const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-    float* recs = a.part + (((int64_t)li * a.Hq + (int64_t)g * G) * a.NC + a.chunk_base + chunk) *
+    float* recs = a.part + (((int64_t)li * a.Hq + (int64_t)g * G) * a.NC + ta.chunk_base + chunk) *
                                (D + 2);
     const int64_t hstride = a.NC * (D + 2);  // between consecutive heads
     if (lane < G) {
@@ -352,12 +426,22 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
     }
 }
 
+// One launch per tier (a single kernel holding all three bodies would need
+// registers for their union): blockIdx.x is the chunk within the tier.
+template <int D, int TIER, int GM>
+__global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
+    __shared__ uint32_t vt[64 * lds_pitch<D>()];
+    __shared__ uint32_t pp[32 * GM];
+    partial_body<D, TIER, GM>(a, a.tier[TIER], blockIdx.x, vt, pp);
+}
+
 // One wavefront per (layer, query head): chunks combined in index order.
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ part, int64_t NC,
                                                    int Hq, float* __restrict__ out,
                                                    float* __restrict__ lse) {
     constexpr int CPL = (D + 63) / 64;  // channels per lane
+    constexpr int U = 4;                // chunks whose loads are in flight together
     const int lane = threadIdx.x;
     const int h = blockIdx.x;
     const int li = blockIdx.y;
@@ -369,14 +453,26 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ par
 #pragma unroll
     for (int k = 0; k < CPL; ++k) acc[k] = 0.0f;
     if (M != -INFINITY) {
-        for (int64_t c = 0; c < NC; ++c) {
-            const float* rec = rec0 + c * (D + 2);
-            const float w = __builtin_amdgcn_exp2f(rec[0] - M);  // 0 for an empty chunk
-            L += w * rec[1];
+        for (int64_t c0 = 0; c0 < NC; c0 += U) {
+            float w[U], l[U], v[U][CPL];
 #pragma unroll
-            for (int k = 0; k < CPL; ++k) {
-                const int ch = lane + 64 * k;
-                if (ch < D) acc[k] += w * rec[2 + ch];
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + u < NC ? c0 + u : NC - 1;
+                const float* rec = rec0 + c * (D + 2);
+                w[u] = c0 + u < NC ? rec[0] : -INFINITY;
+                l[u] = rec[1];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) {
+                    const int ch = lane + 64 * k;
+                    v[u][k] = ch < D ? rec[2 + ch] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float e = __builtin_amdgcn_exp2f(w[u] - M);  // 0 for an empty chunk
+                L += e * l[u];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) acc[k] += e * v[u][k];
             }
         }
     }
@@ -392,8 +488,9 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ par
 
 template <int D, int TIER>
 hipError_t launch_tier(const PartialArgs& a, int nl, int GM, hipStream_t st) {
-    const dim3 grid((unsigned)((a.N + 64 * (int64_t)a.T - 1) / (64 * (int64_t)a.T)), (unsigned)a.H,
-                    (unsigned)nl);
+    const int64_t chunks = a.cend[TIER] - a.tier[TIER].chunk_base;
+    if (chunks == 0) return hipSuccess;
+    const dim3 grid((unsigned)chunks, (unsigned)a.H, (unsigned)nl);
     switch (GM) {
         case 1: decode_partial_kernel<D, TIER, 1><<<grid, 64, 0, st>>>(a); break;
         case 2: decode_partial_kernel<D, TIER, 2><<<grid, 64, 0, st>>>(a); break;
@@ -405,25 +502,14 @@ hipError_t launch_tier(const PartialArgs& a, int nl, int GM, hipStream_t st) {
 }
 
 template <int D>
-hipError_t launch_all(const PartialArgs& base, const TierSeg seg[3], int nl, int GM, float* out,
-                      float* lse, hipStream_t st) {
-    PartialArgs a = base;
-    int64_t cb = 0;
-    for (int t = 0; t < 3; ++t) {
-        const int64_t N = seg[t].count;
-        if (N == 0) continue;
-        a.off_code = seg[t].off_code;
-        a.off_scale = seg[t].off_scale;
-        a.N = N;
-        a.chunk_base = cb;
-        hipError_t e = t == 0 ? launch_tier<D, 0>(a, nl, GM, st)
-                              : (t == 1 ? launch_tier<D, 1>(a, nl, GM, st)
-                                        : launch_tier<D, 2>(a, nl, GM, st));
-        if (e != hipSuccess) return e;
-        cb += (N + 64 * (int64_t)a.T - 1) / (64 * (int64_t)a.T);
-    }
-    merge_kernel<D><<<dim3((unsigned)base.Hq, (unsigned)nl), 64, 0, st>>>(base.part, base.NC,
-                                                                          base.Hq, out, lse);
+hipError_t launch_all(const PartialArgs& a, int nl, int GM, float* out, float* lse,
+                      hipStream_t st) {
+    hipError_t e = launch_tier<D, 1>(a, nl, GM, st);
+    if (e == hipSuccess) e = launch_tier<D, 2>(a, nl, GM, st);
+    if (e == hipSuccess) e = launch_tier<D, 0>(a, nl, GM, st);
+    if (e != hipSuccess) return e;
+    merge_kernel<D><<<dim3((unsigned)a.Hq, (unsigned)nl), 64, 0, st>>>(a.part, a.NC, a.Hq, out,
+                                                                      lse);
     return hipGetLastError();
 }
 
@@ -450,24 +536,31 @@ hipError_t launch_decode(const Dims& s, const TierSeg seg[3], const void* payloa
                          hipStream_t st) {
     PartialArgs a;
     a.payload = static_cast<const uint8_t*>(payload);
-    a.off_code = a.off_scale = 0;
-    a.N = 0;
+    a.T = decode_tiles_per_chunk(s, seg, nl);
+    const int64_t span = 64 * (int64_t)a.T;
+    int64_t cb = 0;
+    for (int t = 0; t < 3; ++t) {
+        a.tier[t].off_code = seg[t].off_code;
+        a.tier[t].off_scale = seg[t].off_scale;
+        a.tier[t].N = seg[t].count;
+        a.tier[t].chunk_base = cb;
+        cb += (seg[t].count + span - 1) / span;
+        a.cend[t] = cb;
+    }
+    a.NC = cb;
     a.H = s.Hkv;
     a.G = s.Hq / s.Hkv;
     a.Hq = s.Hq;
     a.layer0 = layer0;
     a.q = static_cast<const uint16_t*>(q);
     a.part = part;
-    a.chunk_base = 0;
-    a.NC = decode_chunks(s, seg, nl);
-    a.T = decode_tiles_per_chunk(s, seg, nl);
     a.c2 = 1.4426950408889634f / sqrtf((float)s.d);
     int GM = 1;
     while (GM < a.G) GM *= 2;
     switch (s.d) {
-        case 64: return launch_all<64>(a, seg, nl, GM, out, lse, st);
-        case 128: return launch_all<128>(a, seg, nl, GM, out, lse, st);
-        case 256: return launch_all<256>(a, seg, nl, GM, out, lse, st);
+        case 64: return launch_all<64>(a, nl, GM, out, lse, st);
+        case 128: return launch_all<128>(a, nl, GM, out, lse, st);
+        case 256: return launch_all<256>(a, nl, GM, out, lse, st);
         default: return hipErrorInvalidValue;
     }
 }
