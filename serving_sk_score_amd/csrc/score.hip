@@ -41,10 +41,12 @@
 // far above the reference) is redone with the exact update, so the result
 // never overflows whatever the inputs.
 //
-// pass 2 computes S = Q K^T (rows = queries, columns = keys): each lane owns
-// one key column of each 32-key sub-tile, so the column sum is an in-lane
-// accumulation across all query tiles.  A workgroup is one query head and
-// KW wavefronts of 64 stationary keys each; the head's query tiles and their
+// pass 2 computes S^T = K Q^T too, with the wavefront's stationary keys as
+// the A operand: each lane owns one query column (one lse2 value per tile)
+// and 16 key rows of each 32-key sub-tile, whose weights add into 16
+// independent per-lane accumulators across all query tiles; the 32 query
+// lanes are summed once at the end.  A workgroup is one query head and KW
+// wavefronts of 64 stationary keys each; the head's query tiles and their
 // lse2 values stream through LDS and are read by every wavefront.
 //
 // Work is causal (tiles above the diagonal are skipped) and workgroups are
@@ -350,46 +352,29 @@ __global__ __launch_bounds__(W * QW * 64, D == 256 ? 1 : 2) void rowlse_kernel(
 }
 
 // ---------------------------------------------------------------- pass 2 --
-// The 16 per-row values of the C-tile rows held by `lane` (rows crow(e, lane))
-// from a 32-entry LDS vector.
-__device__ __forceinline__ void load_rows(const float* v32, int lane, float (&L)[16]) {
+// Pass 2 computes S^T = K Q^T as well: the stationary keys are the A operand
+// (the same registers a Q K^T layout would use as B), the streamed queries
+// the B operand, so a lane of the C tile owns one query column: one lse value
+// per lane and tile, and 16 key rows whose weights add into 16 independent
+// per-lane column accumulators (summed across the 32 query lanes once, at the
+// end).
+
+// acc[e] += 2^(c2 x_e - L) for the 16 elements of a C tile.
+__device__ __forceinline__ void tile_colacc(const floatx16& a, float L, float c2,
+                                            float (&acc)[16]) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const float4 v = *reinterpret_cast<const float4*>(v32 + 8 * b + 4 * (lane >> 5));
-        L[4 * b + 0] = v.x;
-        L[4 * b + 1] = v.y;
-        L[4 * b + 2] = v.z;
-        L[4 * b + 3] = v.w;
-    }
+    for (int e = 0; e < 16; ++e) acc[e] += ex2(fmaf(a[e], c2, -L));
 }
 
-// Sum over the 16 elements of a pass-2 C tile of 2^(c2 x - L[e]).
-__device__ __forceinline__ float tile_colsum(const floatx16& a, const float (&L)[16], float c2) {
-    float s0 = ex2(fmaf(a[0], c2, -L[0]));
-    float s1 = ex2(fmaf(a[1], c2, -L[1]));
-    float s2 = ex2(fmaf(a[2], c2, -L[2]));
-    float s3 = ex2(fmaf(a[3], c2, -L[3]));
-#pragma unroll
-    for (int e = 4; e < 16; e += 4) {
-        s0 += ex2(fmaf(a[e + 0], c2, -L[e + 0]));
-        s1 += ex2(fmaf(a[e + 1], c2, -L[e + 1]));
-        s2 += ex2(fmaf(a[e + 2], c2, -L[e + 2]));
-        s3 += ex2(fmaf(a[e + 3], c2, -L[e + 3]));
-    }
-    return (s0 + s1) + (s2 + s3);
-}
-
-// Same on a diagonal tile: only rows (queries) at or after the lane's key,
-// i.e. rows crow >= first = key - (first query of the tile).
-__device__ __forceinline__ float tile_colsum_masked(const floatx16& a, const float (&L)[16],
-                                                    float c2, int first, int lane) {
-    float s = 0.0f;
+// Same on a diagonal tile: only keys at or before the lane's query, i.e. key
+// rows crow(e) <= last = query - (first key of the tile).
+__device__ __forceinline__ void tile_colacc_masked(const floatx16& a, float L, float c2, int last,
+                                                   int lane, float (&acc)[16]) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const float p = ex2(fmaf(a[e], c2, -L[e]));
-        s += (crow(e, lane) >= first) ? p : 0.0f;
+        const float p = ex2(fmaf(a[e], c2, -L));
+        acc[e] += (crow(e, lane) <= last) ? p : 0.0f;
     }
-    return s;
 }
 
 template <int D, int KW, int QS>
@@ -452,13 +437,18 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
     }
     __syncthreads();
 
-    float cs[2] = {0.0f, 0.0f};
+    // per key tile t, the column accumulators of the lane's 16 key rows
+    float ca[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ca[t][e] = 0.0f;
     // Software pipeline over the stages after this wavefront's keys: the
-    // column sums of each 32-query unit run while the MFMAs of the next unit
-    // execute.  `pend` starts as -inf with finite row values, which
+    // weights of each 32-query unit are summed while the MFMAs of the next
+    // unit execute.  `pend` starts as -inf with a finite or +inf lse, which
     // contributes exactly zero.
     floatx16 pend[2];
-    const float* pL = lsm;  // finite or +inf values (the first stage's)
+    const float* pL = lsm;  // lse values of the pending unit (the first stage's)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         pend[0][e] = -INFINITY;
@@ -473,18 +463,17 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 floatx16 cur0 = zero16(), cur1 = zero16();
-                const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
+                const _Float16* brow = buf + (32 * u + col) * PITCH + khalf;
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
-                    const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
-                    cur0 = mfma32(a, kf[0][c], cur0);
-                    cur1 = mfma32(a, kf[1][c], cur1);
+                    const half8 b = *reinterpret_cast<const half8*>(brow + c * 16);
+                    cur0 = mfma32(kf[0][c], b, cur0);
+                    cur1 = mfma32(kf[1][c], b, cur1);
                 }
                 {
-                    float L[16];
-                    load_rows(pL, lane, L);
-                    cs[0] += tile_colsum(pend[0], L, c2);
-                    cs[1] += tile_colsum(pend[1], L, c2);
+                    const float L = pL[col];
+                    tile_colacc(pend[0], L, c2, ca[0]);
+                    tile_colacc(pend[1], L, c2, ca[1]);
                 }
                 pend[0] = cur0;
                 pend[1] = cur1;
@@ -499,19 +488,18 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
                 const bool need0 = k0 <= it0 + 31;
                 const bool need1 = k0 + 32 <= it0 + 31;
                 if (!need0) continue;
-                float L[16];
-                load_rows(lb + 32 * u, lane, L);
+                const float L = lb[32 * u + col];
                 floatx16 acc0 = zero16(), acc1 = zero16();
-                const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
+                const _Float16* brow = buf + (32 * u + col) * PITCH + khalf;
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
-                    const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
-                    acc0 = mfma32(a, kf[0][c], acc0);
-                    if (need1) acc1 = mfma32(a, kf[1][c], acc1);
+                    const half8 b = *reinterpret_cast<const half8*>(brow + c * 16);
+                    acc0 = mfma32(kf[0][c], b, acc0);
+                    if (need1) acc1 = mfma32(kf[1][c], b, acc1);
                 }
-                const int first = (int)(k0 - it0) + col;  // key - first query of the tile
-                cs[0] += tile_colsum_masked(acc0, L, c2, first, lane);
-                if (need1) cs[1] += tile_colsum_masked(acc1, L, c2, first + 32, lane);
+                const int last = (int)(it0 - k0) + col;  // query - first key of the tile
+                tile_colacc_masked(acc0, L, c2, last, lane, ca[0]);
+                if (need1) tile_colacc_masked(acc1, L, c2, last - 32, lane, ca[1]);
             }
         }
         if (si + 1 < ns) {
@@ -525,16 +513,24 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
         __syncthreads();
     }
     {
-        float L[16];
-        load_rows(pL, lane, L);
-        cs[0] += tile_colsum(pend[0], L, c2);
-        cs[1] += tile_colsum(pend[1], L, c2);
+        const float L = pL[col];
+        tile_colacc(pend[0], L, c2, ca[0]);
+        tile_colacc(pend[1], L, c2, ca[1]);
     }
+    // sum each key row over the 32 query lanes of its half; lane e of the
+    // half then writes row crow(e)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const float v = cs[t] + __shfl_xor(cs[t], 32, 64);
-        const int64_t j = k0 + 32 * t + col;
-        if (lane < 32 && j < n) partial[(int64_t)h * ldp + j] = v;
+        float mine = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float v = ca[t][e];
+#pragma unroll
+            for (int msk = 16; msk >= 1; msk >>= 1) v += __shfl_xor(v, msk, 64);
+            if (col == e) mine = v;
+        }
+        const int64_t j = k0 + 32 * t + crow(col & 15, lane);
+        if (col < 16 && j < n) partial[(int64_t)h * ldp + j] = mine;
     }
 }
 
