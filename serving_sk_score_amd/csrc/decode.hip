@@ -52,20 +52,9 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <int S>
-__device__ __forceinline__ uint32_t swz_xor_u(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (S << 10));
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
 }
 
@@ -93,8 +82,6 @@ __device__ __forceinline__ void deq4(uint32_t w, h2 s, uint32_t (&o)[4]) {
         o[k] = as_u32(a * s);
     }
 }
-
-constexpr int kPart = 8;  // 16-byte pieces of a row loaded together
 
 // Row bytes per tier and the number of fp16 pairs one 16-byte piece yields.
 template <int D, int TIER>
