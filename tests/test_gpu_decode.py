@@ -206,3 +206,45 @@ def test_decode_needle_at_boundaries(n, H, b):
                 want = OQ.dequantize_rows(codes, s16)[0].astype(np.float64)
             err = np.abs(got[h] - want).max()
             assert err <= 1e-3 * np.abs(want).max(), (j, t, int(slot[j]), h, err)
+
+
+@pytest.mark.parametrize("name", ["qwen25_7b_2tier", "gemma2_9b"])
+def test_decode_full_size_other_shapes(name):
+    """The Qwen2.5-7B-shaped 2-tier request (query groups of 7 heads) and the
+    Gemma-2-9B-shaped one (d = 256, b = 0.3: mostly int4) at full length, all
+    layers in one call; sampled layers against the oracle."""
+    cfg = get_config(name)
+    L, Hq, H, d, n = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.tokens
+    say("full-size decode", name, n)
+    shape = sk.Shape(L, Hq, H, d)
+    pl = sk.plan_make(shape, sk.Policy(n, cfg.sinks, cfg.three_tier, cfg.budget))
+    opl = OP.make_plan(L, Hq, H, d, n, cfg.sinks, cfg.budget, cfg.three_tier)
+    _, _, amap, _ = OA.assign(tied_scores(4, n), opl.n16, opl.n8, opl.n4, opl.sinks)
+    layers = sorted({1, L - 2})
+    Kd = torch.empty((L, n, H, d), dtype=torch.float16, device="cuda")
+    Vd = torch.empty_like(Kd)
+    hk, hv = {}, {}
+    for layer in range(L):
+        k, v = gen.keys(cfg, layer), gen.values(cfg, layer)
+        Kd[layer].copy_(torch.from_numpy(k))
+        Vd[layer].copy_(torch.from_numpy(v))
+        if layer in layers:
+            hk[layer], hv[layer] = k, v
+    md = to_dev(amap.view(np.int32))
+    payload = torch.empty(pl.payload_bytes, dtype=torch.uint8, device="cuda")
+    sk.pack(shape, pl, Kd, Vd, md, None, payload)
+    del Kd, Vd
+    rng = np.random.default_rng(10)
+    q = (rng.standard_normal((L, Hq, d)) * 0.5).astype(np.float16)
+    o = torch.empty((L, Hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((L, Hq), dtype=torch.float32, device="cuda")
+    sk.decode_attention(shape, pl, payload, to_dev(q), o, lse)
+    torch.cuda.synchronize()
+    og, lg = o.cpu().numpy(), lse.cpu().numpy()
+    one = OP.make_plan(1, Hq, H, d, n, cfg.sinks, cfg.budget, cfg.three_tier)
+    for layer in layers:
+        say("checking layer", layer)
+        ph = OQ.pack(hk[layer][None], hv[layer][None], amap, one)
+        wo, wl = OD.layer_attention(ph, amap, one, 0, H, d, q[layer])
+        vmax = _vmax(ph, amap, one, [0], H, d, Hq)
+        _check(og[layer][None], lg[layer][None], wo[None], wl[None], vmax, f"{name} layer {layer}")
