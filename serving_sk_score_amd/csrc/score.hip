@@ -378,7 +378,7 @@ __device__ __forceinline__ void tile_colacc_masked(const floatx16& a, float L, f
 }
 
 template <int D, int KW, int QS>
-__global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
+__global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
     const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     const float* __restrict__ lse2, float* __restrict__ partial, int64_t n, int64_t ldp, int Hq,
     int Hkv, float c2) {
@@ -446,7 +446,11 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
     // Software pipeline over the stages after this wavefront's keys: the
     // weights of each 32-query unit are summed while the MFMAs of the next
     // unit execute.  `pend` starts as -inf with a finite or +inf lse, which
-    // contributes exactly zero.
+    // contributes exactly zero.  At d = 256 the MFMAs of a unit take twice
+    // its softmax time and the 32 registers of the pending tiles would leave
+    // one wavefront per SIMD, so there each unit is summed right after its
+    // own MFMAs and the two wavefronts of a SIMD overlap each other instead.
+    constexpr bool kPipe = D != 256;
     floatx16 pend[2];
     const float* pL = lsm;  // lse values of the pending unit (the first stage's)
 #pragma unroll
@@ -470,14 +474,18 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
                     cur0 = mfma32(kf[0][c], b, cur0);
                     cur1 = mfma32(kf[1][c], b, cur1);
                 }
-                {
+                if constexpr (kPipe) {
                     const float L = pL[col];
                     tile_colacc(pend[0], L, c2, ca[0]);
                     tile_colacc(pend[1], L, c2, ca[1]);
+                    pend[0] = cur0;
+                    pend[1] = cur1;
+                    pL = lb + 32 * u;
+                } else {
+                    const float L = lb[32 * u + col];
+                    tile_colacc(cur0, L, c2, ca[0]);
+                    tile_colacc(cur1, L, c2, ca[1]);
                 }
-                pend[0] = cur0;
-                pend[1] = cur1;
-                pL = lb + 32 * u;
             }
         } else if (s0 + QS > k0) {
             // the stage crosses this wavefront's keys: causal mask (these
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(KW * 64, D == 256 ? 1 : 2) void colsum_kernel(
         }
         __syncthreads();
     }
-    {
+    if constexpr (kPipe) {
         const float L = pL[col];
         tile_colacc(pend[0], L, c2, ca[0]);
         tile_colacc(pend[1], L, c2, ca[1]);
