@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="mistral7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-score-shapes", action="store_true",
+                    help="skip timing the score passes on one Qwen- and one Gemma-shaped layer")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough budget of the oracle's timed sample")
     return ap.parse_args()
@@ -229,6 +231,37 @@ def main():
     dec_bytes = plan.payload_bytes + dec_io
     dec16_bytes = plan16.payload_bytes + dec_io
 
+    # the score passes on one layer of each long-context workload's shape
+    # (seeded inputs of that workload): parity cases, not bench lines, timed
+    # here so the line shows the passes at their other head counts and d
+    score_shapes = {}
+    if not args.no_score_shapes:
+        for other in ("qwen25_7b_2tier", "gemma2_9b"):
+            oc = get_config(other)
+            ok_ = gen.keys(oc, 0)
+            oq = torch.from_numpy(gen.queries(oc, 0, k=ok_)).to(dev)
+            ok_ = torch.from_numpy(ok_).to(dev)
+            osh = sk.Shape(1, oc.q_heads, oc.kv_heads, oc.head_dim)
+            on = oc.tokens
+            olse = torch.empty((oc.q_heads, on), dtype=torch.float32, device=dev)
+            osc = torch.empty(on, dtype=torch.float32, device=dev)
+            ows = torch.empty(max(1, sk.colsum_workspace_bytes(osh, on)), dtype=torch.uint8,
+                              device=dev)
+            t_r = timed(lambda: sk.score_rowlse(osh, oq, ok_, olse), 3)
+            t_c = timed(lambda: sk.score_colsum(osh, oq, ok_, olse, osc, False, ows), 3)
+            f = oc.q_heads * oc.head_dim * on * (on + 1)
+            names = score_kernel_names(oc.q_heads, oc.kv_heads, oc.head_dim)
+            score_shapes[other] = {
+                "layer": f"Hq={oc.q_heads} Hkv={oc.kv_heads} d={oc.head_dim} n={on}",
+                "rowlse": {"kernel": names["rowlse"], "ms": round(t_r, 4),
+                           "tflops": round(f / (t_r * 1e-3) / 1e12, 1),
+                           "frac": round(f / (t_r * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+                "colsum": {"kernel": names["colsum"], "ms": round(t_c, 4),
+                           "tflops": round(f / (t_c * 1e-3) / 1e12, 1),
+                           "frac": round(f / (t_c * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}}
+            del oq, ok_, olse, osc, ows
+            log(f"score passes on one {other} layer: {t_r:.3f} + {t_c:.3f} ms")
+
     # per stage: [steps][launches] durations in ms
     t = {s: np.array([[e[s][2 * j].elapsed_time(e[s][2 * j + 1]) for j in range(len(e[s]) // 2)]
                       for e in all_ev]) for s in stages}
@@ -315,6 +348,7 @@ def main():
                    "fp16_payload": call_rl(dec16_bytes, t_dec16),
                    "ms": round(t_dec * 1e3, 4), "fp16_ms": round(t_dec16 * 1e3, 4),
                    "speedup_vs_fp16": round(t_dec16 / t_dec, 3)},
+        "score_other_shapes": score_shapes,
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "copy_bytes": int(src.numel()),
         "wall_s_timed": round(wall, 3),
@@ -326,12 +360,12 @@ def main():
 
 def score_kernel_names(Hq, Hkv, d):
     """Template instances the library launches for this shape (the rule of
-    its launchers: W = largest divisor of Hq/Hkv up to 8 heads per row-pass
-    workgroup, QW = 4/W blocks of 64 queries when W < 3, stages of 64 rows,
+    its launchers: W = the largest of 4, 2, 1 dividing Hq/Hkv heads per
+    row-pass workgroup, QW = 4/W blocks of 64 queries, stages of 64 rows,
     32 at d = 256; the column pass uses 4 wavefronts)."""
     R = Hq // Hkv
-    W = max(w for w in range(1, 9) if R % w == 0)
-    QW = 1 if W >= 3 else 4 // W
+    W = next(w for w in (4, 2, 1) if R % w == 0)
+    QW = 4 // W
     KS = 32 if d == 256 else 64
     return {"rowlse": f"rowlse_kernel<{d},{W},{QW},{KS}>",
             "colsum": f"colsum_kernel<{d},4,{KS}>"}
