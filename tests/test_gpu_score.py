@@ -49,6 +49,10 @@ def _close(got, want, tag):
     (6, 33, 2, 1, 64, 1.0), (7, 64, 8, 2, 128, 1.0), (8, 65, 8, 2, 128, 1.0),
     (9, 1500, 32, 8, 128, 1.0), (10, 400, 28, 4, 128, 1.0), (11, 640, 4, 1, 128, 3.0),
     (12, 129, 6, 2, 64, 2.0), (13, 96, 16, 1, 64, 1.0),
+    # row-pass workgroups of 4 heads in 2 chunks per group, 2 heads in 3
+    # chunks, and 1 head x 4 query blocks at d = 256; 4 heads at d = 256
+    (14, 450, 16, 2, 128, 1.0), (15, 300, 12, 2, 64, 1.0), (16, 257, 5, 1, 256, 1.0),
+    (17, 700, 8, 2, 256, 1.0),
 ])
 def test_score_random(seed, n, Hq, Hkv, d, scale):
     say("score", dict(n=n, Hq=Hq, Hkv=Hkv, d=d, scale=scale))
