@@ -157,7 +157,9 @@ sk_status sk_plan_make(const sk_shape* shape, const sk_policy* policy, sk_plan* 
  * Two passes run back to back on `stream`: a row log-sum-exp pass and a
  * column-sum pass that recomputes q.k with MFMA and sums exp(s - lse); the
  * per-query-head partial sums are then added in a fixed order, so the
- * result is deterministic. */
+ * result is deterministic.  The score calls (this one, sk_score_rowlse and
+ * sk_score_colsum) take n_tokens <= 4,194,240 (65535 blocks of 64 queries);
+ * a longer request returns SK_E_UNSUPPORTED. */
 size_t    sk_score_workspace_bytes(const sk_shape* shape, int64_t n_tokens);
 sk_status sk_score(const sk_shape* shape, int64_t n_tokens,
                    const void* q, const void* k, float* score, int32_t accumulate,

@@ -212,9 +212,16 @@ size_t sk_score_workspace_bytes(const sk_shape* shape, int64_t n) {
     return lse_bytes(shape, n) + partial_bytes(shape, n);
 }
 
+// The row pass launches one workgroup row per 64 queries (for four heads per
+// workgroup) and a launch grid holds at most 65535 rows.
+constexpr int64_t kMaxScoreTokens = (int64_t)65535 * 64;
+
 static sk_status check_score_io(const sk_shape* shape, int64_t n, const void* q, const void* k) {
     if (sk_status st = check_shape(shape)) return st;
     if (sk_status st = check_tokens(n)) return st;
+    if (n > kMaxScoreTokens)
+        return fail(SK_E_UNSUPPORTED, "score: n_tokens %lld above %lld", (long long)n,
+                    (long long)kMaxScoreTokens);
     if (n > 0 && (!q || !k)) return fail(SK_E_ARG, "q and k must be non-NULL");
     if (!aligned(q, 16) || !aligned(k, 16)) return fail(SK_E_ARG, "q and k must be 16-byte aligned");
     return SK_OK;

@@ -126,6 +126,10 @@ def test_call_validation_without_device():
     assert lib.sk_score_rowlse(B(shape), 100, FAKE, FAKE, None, None) == sk.SK_E_ARG
     bad_shape, _ = _c((2, 4, 2, 80))
     assert lib.sk_score(B(bad_shape), 100, FAKE, FAKE, FAKE, 0, FAKE, need, None) == sk.SK_E_UNSUPPORTED
+    # longer than the launch grid of the row pass holds (65535 blocks of 64)
+    big = 65535 * 64 + 1
+    assert lib.sk_score_rowlse(B(shape), big, FAKE, FAKE, FAKE, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_score(B(shape), big, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == sk.SK_E_UNSUPPORTED
     # empty request: OK and nothing touched even with NULL buffers
     assert lib.sk_score(B(shape), 0, None, None, None, 0, None, 0, None) == sk.SK_OK
     assert lib.sk_score_rowlse(B(shape), 0, None, None, None, None) == sk.SK_OK
