@@ -289,7 +289,7 @@ def main():
         gbs = bytes_ / sec / 1e9
         return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": bytes_,
-                "traffic": counted_traffic(kernel)}
+                "traffic": counted_traffic(kernel, cfg.name)}
 
     def call_rl(bytes_, sec):
         gbs = bytes_ / sec / 1e9
@@ -326,7 +326,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": kernel_name, "achieved": round(ach, 1),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": counted_traffic(kernel_name),
+                     "traffic": counted_traffic(kernel_name, cfg.name),
                      "flops_per_launch": pass_flops,
                      "avg_launch_ms": round(mean_launch[dom], 4)},
         "roofline_stages": {"pack": rl(pack_bytes, t_pack, f"pack_kernel<{d},{nb}>"),
@@ -382,25 +382,27 @@ def pack_batch(Hkv, d):
     return nb
 
 
-def counted_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summaries (FETCH_SIZE + WRITE_SIZE, calibrated against a device copy), or
-    None when no summary covers it or its source file changed since."""
+def counted_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summaries (FETCH_SIZE + WRITE_SIZE, calibrated against a
+    device copy), or None when no summary covers it or its source file changed
+    since."""
     import glob
     import hashlib
     import re
 
     root = os.path.dirname(os.path.abspath(__file__))
-    pat = re.compile(r"<!-- traffic kernel=(\S+) bytes_per_launch=(\d+) source=(\S+) sha256=([0-9a-f]+) -->")
+    pat = re.compile(r"<!-- traffic workload=(\S+) kernel=(\S+) bytes_per_launch=(\d+) "
+                     r"source=(\S+) sha256=([0-9a-f]+) -->")
     for path in sorted(glob.glob(os.path.join(root, "profiles", "*.md"))):
         for m in pat.finditer(open(path).read()):
-            if m.group(1) != kernel:
+            if m.group(1) != workload or m.group(2) != kernel:
                 continue
-            src = os.path.join(root, m.group(3))
+            src = os.path.join(root, m.group(4))
             if not os.path.exists(src):
                 continue
-            if hashlib.sha256(open(src, "rb").read()).hexdigest() == m.group(4):
-                return int(m.group(2))
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() == m.group(5):
+                return int(m.group(3))
     return None
 
 
