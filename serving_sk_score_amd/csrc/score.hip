@@ -525,20 +525,39 @@ __global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
         tile_colacc(pend[0], L, c2, ca[0]);
         tile_colacc(pend[1], L, c2, ca[1]);
     }
-    // sum each key row over the 32 query lanes of its half; lane e of the
-    // half then writes row crow(e)
+    // sum each key row over the 32 query lanes of its half by a transpose
+    // reduction: at the exchange with lane ^ m (m = 16, 8, 4, 2) a lane keeps
+    // one half of its remaining rows (the upper half when lane & m) and adds
+    // its partner's copy of them, so 8 + 4 + 2 + 1 exchanges leave row
+    // e = (lane >> 1) & 15 summed over 16 lanes, and a last exchange with
+    // lane ^ 1 completes it; the even lanes of each half write their row
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        float mine = 0.0f;
+        float r8[8], r4[4], r2[2];
+        const bool u16 = (col & 16) != 0, u8 = (col & 8) != 0, u4 = (col & 4) != 0,
+                   u2 = (col & 2) != 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            float v = ca[t][e];
-#pragma unroll
-            for (int msk = 16; msk >= 1; msk >>= 1) v += __shfl_xor(v, msk, 64);
-            if (col == e) mine = v;
+        for (int i = 0; i < 8; ++i) {
+            const float keep = u16 ? ca[t][i + 8] : ca[t][i];
+            const float send = u16 ? ca[t][i] : ca[t][i + 8];
+            r8[i] = keep + __shfl_xor(send, 16, 64);
         }
-        const int64_t j = k0 + 32 * t + crow(col & 15, lane);
-        if (col < 16 && j < n) partial[(int64_t)h * ldp + j] = mine;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float keep = u8 ? r8[i + 4] : r8[i];
+            const float send = u8 ? r8[i] : r8[i + 4];
+            r4[i] = keep + __shfl_xor(send, 8, 64);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float keep = u4 ? r4[i + 2] : r4[i];
+            const float send = u4 ? r4[i] : r4[i + 2];
+            r2[i] = keep + __shfl_xor(send, 4, 64);
+        }
+        float v = (u2 ? r2[1] : r2[0]) + __shfl_xor(u2 ? r2[0] : r2[1], 2, 64);
+        v += __shfl_xor(v, 1, 64);
+        const int64_t j = k0 + 32 * t + crow((col >> 1) & 15, lane);
+        if ((col & 1) == 0 && j < n) partial[(int64_t)h * ldp + j] = v;
     }
 }
 
