@@ -111,9 +111,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // halfs puts the 32 rows of an MFMA fragment read at distinct bank groups.
 // Each thread owns the same 16-byte pieces in every stage: its first piece
 // at a fixed per-thread offset, the others a uniform number of rows further
-// (an SGPR offset for the buffer load, an immediate for the LDS store).  The
-// stage's buffer resource covers only its tokens below n, so the range check
-// zero-fills the ragged tail.
+// (an immediate for the LDS store).  The stage's buffer resource covers only
+// its tokens below n, and each load's whole offset is in its per-lane VGPR
+// offset (the part the range check always covers), so the check zero-fills
+// the ragged tail.
 template <int D, int ROWS, int NT>
 struct Stager {
     static constexpr int kPieces = D / 8;           // 16-byte pieces per row
@@ -130,15 +131,19 @@ struct Stager {
         voff = (uint32_t)((row0 * gstride + piece * 8) * 2);
         loff = row0 * (D + 8) + piece * 8;
     }
-    // g points at token t0 of this head's rows; n_left = n - t0 > 0.
+    // g points at token t0 of this head's rows; n_left = n - t0 > 0.  The
+    // range ends at the last byte of the stage's last valid row of this head
+    // (not at that token's stride end, which for any head but the last lies
+    // inside the next head's row and, for the last, past the tensor).
     __device__ __forceinline__ void load(const _Float16* g, int64_t n_left, int64_t gstride) {
         const int64_t rows = n_left < ROWS ? n_left : ROWS;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(g, (uint32_t)(rows * gstride * 2));
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(g, (uint32_t)(((rows - 1) * gstride + D) * 2));
 #pragma unroll
         for (int r = 0; r < kRegs; ++r) {
             if (ROWS % kRowStep == 0 || row0 + r * kRowStep < ROWS) {
                 const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, voff, (int)(r * kRowStep * gstride * 2), 0);
+                    rs, voff + (uint32_t)(r * kRowStep * gstride * 2), 0, 0);
                 regs[r] = *reinterpret_cast<const uint4*>(&v);
             }
         }

@@ -20,13 +20,14 @@ struct TierSeg {
     int64_t off_scale; // byte offset of the scale segment (int tiers)
 };
 
-// score pass 1: lse fp32 [Hq][n] (natural log)
+// score pass 1: lse fp32 [Hq][n], base-2 log of the causal softmax denominator
 hipError_t launch_rowlse(const Dims& s, const void* q, const void* k, float* lse,
                          hipStream_t st);
-// score pass 2: partial fp32 [Hkv][n_pad], n_pad = padded_tokens(n)
+// score pass 2: per-query-head column sums, partial fp32 [Hq][n_pad],
+// n_pad = padded_tokens(n)
 hipError_t launch_colsum(const Dims& s, const void* q, const void* k, const float* lse,
                          float* partial, hipStream_t st);
-// score[j] = (acc ? score[j] : 0) + sum_g partial[g][j], g in order
+// score[j] = (acc ? score[j] : 0) + sum_h partial[h][j], h in order
 hipError_t launch_reduce(const Dims& s, const float* partial, float* score, int acc,
                          hipStream_t st);
 int64_t padded_tokens(int64_t n);
