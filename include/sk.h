@@ -19,7 +19,8 @@
  *   - Ownership: the caller allocates and frees every buffer.  The library
  *     never allocates, frees or synchronizes, and keeps no pointer after a
  *     call returns.  It has no global mutable state except the per-thread
- *     error message.
+ *     error message and the static per-device scratch of sk_score_noalloc
+ *     (with its looked-up addresses).
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *     stream).  Device work is enqueued asynchronously on it.
  *   - Validation: all arguments are checked on the host before anything is
@@ -164,6 +165,26 @@ size_t    sk_score_workspace_bytes(const sk_shape* shape, int64_t n_tokens);
 sk_status sk_score(const sk_shape* shape, int64_t n_tokens,
                    const void* q, const void* k, float* score, int32_t accumulate,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free variant of sk_score, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and error behaviour as
+ * sk_score, without the workspace: the lse values and per-head column sums
+ * live in a static device array of SK_SCORE_SCRATCH_BYTES that the library
+ * owns, one per GPU it runs on, held until the process ends (its address is
+ * looked up on the first call on each device; a failed lookup returns
+ * SK_E_DEVICE).  A request needing more than that
+ * (sk_score_workspace_bytes(shape, n) > SK_SCORE_SCRATCH_BYTES, i.e. about
+ * n_q_heads * n_tokens > 4.19M) returns SK_E_WORKSPACE before anything is
+ * enqueued.  Nothing needs clearing between calls (every scratch byte a call
+ * reads, that call wrote first), but all calls on one GPU share the array:
+ * calls that overlap in time on one GPU (on different streams, or from
+ * different host threads without ordering) race and give wrong results.
+ * The call itself allocates and frees nothing. */
+#define SK_SCORE_SCRATCH_BYTES ((size_t)32 << 20)
+sk_status sk_score_noalloc(const sk_shape* shape, int64_t n_tokens,
+                           const void* q, const void* k, float* score, int32_t accumulate,
+                           void* stream);
 
 /* The two passes of sk_score as separate calls (same results when chained).
  *   sk_score_rowlse : lse fp32 [n_q_heads][n], the base-2 logarithm of the

@@ -7,10 +7,11 @@ Python binding; PyTorch only provides device memory and streams.
 """
 
 from .sk import (  # noqa: F401
-    OVERFLOW_DROP, OVERFLOW_FALLBACK, OVERFLOW_REJECT, TIER_DROP, Plan, Policy, Shape,
+    OVERFLOW_DROP, OVERFLOW_FALLBACK, OVERFLOW_REJECT, SCORE_SCRATCH_BYTES, SK_E_WORKSPACE,
+    TIER_DROP, Plan, Policy, Shape,
     SkError, assign_tiers, balanced_keys, colsum_workspace_bytes, decode_attention,
     decode_workspace_bytes, lib, pack,
-    plan_make, recency_weight, score, score_colsum, score_kvnorm, score_rowlse,
+    plan_make, recency_weight, score, score_colsum, score_kvnorm, score_noalloc, score_rowlse,
     score_workspace_bytes, unpack, unpack_paged, upgrade_bytes, upgrade_pack, upgrade_unpack,
     upgrade_unpack_paged,
 )

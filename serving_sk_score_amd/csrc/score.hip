@@ -55,9 +55,20 @@
 // its own L2.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
+#include "../../include/sk.h"
 #include "sk_kernels.h"
+
+// Workspace of sk_score_noalloc (lse values, then the per-head column sums):
+// a device array the library owns, so that a caller that cannot allocate
+// needs no workspace.  Each GPU the library runs on holds its own copy until
+// the process ends.  In host code this name is only a stand-in for the
+// symbol, not a device address: the address comes from hipGetSymbolAddress,
+// once per device (score_scratch below), and only that address is passed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[SK_SCORE_SCRATCH_BYTES];
 
 namespace sk {
 namespace {
@@ -673,5 +684,29 @@ hipError_t launch_reduce(const Dims& s, const float* partial, float* score, int 
 }
 
 int colsum_partial_rows(const Dims& s) { return s.Hq; }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t score_scratch(void** ptr, size_t* bytes) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
 
 }  // namespace sk

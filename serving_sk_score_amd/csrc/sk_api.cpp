@@ -257,17 +257,19 @@ sk_status sk_score_colsum(const sk_shape* shape, int64_t n, const void* q, const
                   "reduce");
 }
 
-sk_status sk_score(const sk_shape* shape, int64_t n, const void* q, const void* k, float* score,
-                   int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+static sk_status check_score_call(const sk_shape* shape, int64_t n, const void* q,
+                                   const void* k, const float* score, int32_t accumulate) {
     if (sk_status st = check_score_io(shape, n, q, k)) return st;
     if (n > 0 && !score) return fail(SK_E_ARG, "score must be non-NULL");
     if (!aligned(score, 4)) return fail(SK_E_ARG, "score must be 4-byte aligned");
     if (accumulate != 0 && accumulate != 1) return fail(SK_E_ARG, "accumulate must be 0 or 1");
-    if (n == 0) return ok();
-    const size_t need = lse_bytes(shape, n) + partial_bytes(shape, n);
-    if (!ws || ws_bytes < need)
-        return fail(SK_E_WORKSPACE, "score workspace needs %zu bytes, got %zu", need, ws_bytes);
-    if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");
+    return SK_OK;
+}
+
+// The three launches of a score call over a validated workspace of
+// lse_bytes + partial_bytes bytes.
+static sk_status run_score(const sk_shape* shape, int64_t n, const void* q, const void* k,
+                           float* score, int32_t accumulate, void* ws, void* stream) {
     const sk::Dims d = dims(shape, n);
     float* lse = (float*)ws;
     float* partial = (float*)((char*)ws + lse_bytes(shape, n));
@@ -278,6 +280,35 @@ sk_status sk_score(const sk_shape* shape, int64_t n, const void* q, const void* 
     e = sk::launch_colsum(d, q, k, lse, partial, st);
     if (e != hipSuccess) return device(e, "colsum");
     return device(sk::launch_reduce(d, partial, score, accumulate, st), "reduce");
+}
+
+sk_status sk_score(const sk_shape* shape, int64_t n, const void* q, const void* k, float* score,
+                   int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+    if (sk_status st = check_score_call(shape, n, q, k, score, accumulate)) return st;
+    if (n == 0) return ok();
+    const size_t need = lse_bytes(shape, n) + partial_bytes(shape, n);
+    if (!ws || ws_bytes < need)
+        return fail(SK_E_WORKSPACE, "score workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");
+    return run_score(shape, n, q, k, score, accumulate, ws, stream);
+}
+
+sk_status sk_score_noalloc(const sk_shape* shape, int64_t n, const void* q, const void* k,
+                           float* score, int32_t accumulate, void* stream) {
+    if (sk_status st = check_score_call(shape, n, q, k, score, accumulate)) return st;
+    if (n == 0) return ok();
+    const size_t need = lse_bytes(shape, n) + partial_bytes(shape, n);
+    if (need > SK_SCORE_SCRATCH_BYTES)
+        return fail(SK_E_WORKSPACE,
+                    "sk_score_noalloc: n_q_heads %d x n_tokens %lld needs %zu scratch bytes, "
+                    "the static scratch holds %zu; use sk_score with a workspace",
+                    shape->n_q_heads, (long long)n, need, (size_t)SK_SCORE_SCRATCH_BYTES);
+    void* ws = nullptr;
+    size_t have = 0;
+    hipError_t e = sk::score_scratch(&ws, &have);
+    if (e != hipSuccess) return device(e, "score scratch lookup");
+    if (have < need) return fail(SK_E_WORKSPACE, "score scratch holds %zu bytes", have);
+    return run_score(shape, n, q, k, score, accumulate, ws, stream);
 }
 
 sk_status sk_recency_weight(int64_t n, double lambda, const float* in, float* out,

@@ -31,6 +31,9 @@ hipError_t launch_colsum(const Dims& s, const void* q, const void* k, const floa
 hipError_t launch_reduce(const Dims& s, const float* partial, float* score, int acc,
                          hipStream_t st);
 int64_t padded_tokens(int64_t n);
+// Device address and size of the static score workspace on the current
+// device (looked up once per device).
+hipError_t score_scratch(void** ptr, size_t* bytes);
 // number of rows of the pass-2 partial buffer
 int colsum_partial_rows(const Dims& s);
 

@@ -26,8 +26,10 @@ EXPORTS = [
     "sk_assign_tiers", "sk_pack", "sk_unpack", "sk_status_string", "sk_last_error",
     "sk_layout_version", "sk_recency_weight", "sk_score_kvnorm", "sk_upgrade_bytes",
     "sk_upgrade_pack", "sk_upgrade_unpack", "sk_balanced_keys", "sk_decode_workspace_bytes",
-    "sk_decode_attention",
+    "sk_decode_attention", "sk_score_noalloc",
 ]
+
+SCORE_SCRATCH_BYTES = 32 << 20   # SK_SCORE_SCRATCH_BYTES
 
 
 class SkError(RuntimeError):
@@ -106,6 +108,7 @@ def lib():
             "sk_plan_make": (i32, [P(_Shape), P(_Policy), P(_Plan)]),
             "sk_score_workspace_bytes": (sz, [P(_Shape), i64]),
             "sk_score": (i32, [P(_Shape), i64, vp, vp, vp, i32, vp, sz, vp]),
+            "sk_score_noalloc": (i32, [P(_Shape), i64, vp, vp, vp, i32, vp]),
             "sk_score_rowlse": (i32, [P(_Shape), i64, vp, vp, vp, vp]),
             "sk_score_colsum_workspace_bytes": (sz, [P(_Shape), i64]),
             "sk_score_colsum": (i32, [P(_Shape), i64, vp, vp, vp, vp, i32, vp, sz, vp]),
@@ -211,6 +214,15 @@ def score(shape: Shape, q, k, out, accumulate=False, ws=None):
     _need(ws, "ws", torch.uint8, numel=need)
     _check(lib().sk_score(ctypes.byref(shape.c()), n, _ptr(q), _ptr(k), _ptr(out),
                           int(bool(accumulate)), _ptr(ws), ws.numel(), _stream(q)))
+    return out
+
+
+def score_noalloc(shape: Shape, q, k, out, accumulate=False):
+    """sk_score without a workspace (the library's static scratch is used)."""
+    n = _qk(shape, q, k)
+    _need(out, "score", torch.float32, shape=(n,))
+    _check(lib().sk_score_noalloc(ctypes.byref(shape.c()), n, _ptr(q), _ptr(k), _ptr(out),
+                                  int(bool(accumulate)), _stream(q)))
     return out
 
 

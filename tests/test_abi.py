@@ -130,6 +130,18 @@ def test_call_validation_without_device():
     big = 65535 * 64 + 1
     assert lib.sk_score_rowlse(B(shape), big, FAKE, FAKE, FAKE, None) == sk.SK_E_UNSUPPORTED
     assert lib.sk_score(B(shape), big, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == sk.SK_E_UNSUPPORTED
+    # allocation-free score: same argument checks, and a request larger than
+    # the static scratch is rejected before any device is touched
+    assert lib.sk_score_noalloc(B(shape), 100, None, FAKE, FAKE, 0, None) == sk.SK_E_ARG
+    assert lib.sk_score_noalloc(B(shape), 100, FAKE, FAKE, FAKE, 2, None) == sk.SK_E_ARG
+    assert lib.sk_score_noalloc(B(bad_shape), 100, FAKE, FAKE, FAKE, 0, None) == sk.SK_E_UNSUPPORTED
+    wide, _ = _c((1, 32, 8, 128))
+    for n_big in (131073, 1 << 20):
+        assert lib.sk_score_workspace_bytes(B(wide), n_big) > sk.SCORE_SCRATCH_BYTES
+        assert lib.sk_score_noalloc(B(wide), n_big, FAKE, FAKE, FAKE, 0, None) == sk.SK_E_WORKSPACE
+        assert b"scratch" in lib.sk_last_error()
+    assert lib.sk_score_workspace_bytes(B(wide), 131072) == sk.SCORE_SCRATCH_BYTES
+    assert lib.sk_score_noalloc(B(shape), 0, None, None, None, 0, None) == sk.SK_OK
     # empty request: OK and nothing touched even with NULL buffers
     assert lib.sk_score(B(shape), 0, None, None, None, 0, None, 0, None) == sk.SK_OK
     assert lib.sk_score_rowlse(B(shape), 0, None, None, None, None) == sk.SK_OK
