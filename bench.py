@@ -1,19 +1,27 @@
 """Benchmark of the mixed-precision KV transfer path on one MI355X.
 
-One step = the whole path over one request of the Mistral-7B-shaped workload
-(32 layers, 32 query / 8 KV heads, head dim 128, 8192 tokens, S = 4 sinks,
-3-tier, b = 0.5): per layer the two score passes (row log-sum-exp, then the
-MFMA column sums accumulated into the score), tier assignment, pack, dense
-unpack and paged unpack (16-token blocks, seeded permuted block table).
-Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+One step = the whole path over the batched serving mix, the largest workload
+that fits one GPU: 16 Mistral-7B-shaped requests (32 layers, 32 query / 8 KV
+heads, head dim 128) with seeded log-uniform lengths in [1024, 65536]
+(277,716 tokens), S = 4 sinks, 3-tier.  Per request and layer the two score
+passes (row log-sum-exp, then the MFMA column sums accumulated into the
+request's score); then, at each budget of the sweep b in {0.3, 0.5, 0.7}, the
+tier assignment of every request, the pack of every request, and the paged
+unpack of every request into one shared fp16 cache of 16-token blocks under a
+seeded permuted block table.  Inputs are seeded synthetic tensors drawn on
+the device (workloads.gen_device), resident in HBM before timing starts.
 
-Prints one JSON line.  ``value`` is the fp16-equivalent KV throughput of
-pack + dense unpack, 2 * KV_fp16_bytes / (t_pack + t_unpack), from HIP events
-recorded on the launch stream inside the timed steps; the score's TFLOP/s and
-every stage's time are reported beside it.
+Prints one JSON line.  ``value`` is the fp16-equivalent KV throughput of pack
++ unpack over the step, sum(2 * KV_fp16_bytes) / sum(t_pack + t_unpack) over
+every request and budget, from HIP events recorded on the launch stream
+around every launch inside the timed steps; the score's TFLOP/s and every
+stage's time are reported beside it.  The single-request workloads
+(Gemma-2-9B-, Qwen2.5-7B- and Mistral-7B-shaped) follow under ``workloads``,
+each as its own whole-path measurement with its own rooflines.
 """
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -23,6 +31,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "KV pack+unpack GB/s (fp16-equiv, % HBM peak); importance-score TFLOP/s"
 
 
 def parse():
@@ -30,11 +39,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="mistral7b")
+    ap.add_argument("--workload", default="batched_mix",
+                    help="the headline workload (batched_mix, or a single-request one)")
+    ap.add_argument("--others", default="gemma2_9b,qwen25_7b_2tier,mistral7b",
+                    help="comma-separated single-request workloads measured after the "
+                         "headline ('' for none)")
+    ap.add_argument("--other-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-score-shapes", action="store_true",
-                    help="skip timing the score passes on one Qwen- and one Gemma-shaped layer")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough budget of the oracle's timed sample")
     return ap.parse_args()
 
@@ -43,319 +55,32 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the transfer path is built and timed on a "
-              "single MI355X (multi-GPU sharding is a design note, not a measured path).",
-              file=sys.stderr)
-        sys.exit(2)
+class Marks:
+    """HIP events around every launch of a step, on the launch stream."""
 
-    import torch
-    import serving_sk_score_amd as sk
-    from workloads import gen, get_config
+    def __init__(self, torch):
+        self.torch = torch
+        self.rec = []
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    sk.lib()  # fails loudly if the HIP library is not built
-
-    cfg = get_config(args.workload)
-    L, Hq, Hkv, d, n = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.tokens
-    dev = torch.device("cuda", 0)
-    log(f"workload {cfg.name}: L={L} Hq={Hq} Hkv={Hkv} d={d} n={n}; generating inputs")
-    t0 = time.time()
-    from concurrent.futures import ThreadPoolExecutor
-
-    Q = torch.empty((L, n, Hq, d), dtype=torch.float16, device=dev)
-    K = torch.empty((L, n, Hkv, d), dtype=torch.float16, device=dev)
-    V = torch.empty((L, n, Hkv, d), dtype=torch.float16, device=dev)
-
-    def layer_inputs(layer):
-        k = gen.keys(cfg, layer)
-        return gen.queries(cfg, layer, k=k), k, gen.values(cfg, layer)
-
-    with ThreadPoolExecutor(16) as ex:
-        for layer, (q, k, v) in enumerate(ex.map(layer_inputs, range(L))):
-            Q[layer].copy_(torch.from_numpy(q))
-            K[layer].copy_(torch.from_numpy(k))
-            V[layer].copy_(torch.from_numpy(v))
-    torch.cuda.synchronize()
-    log(f"inputs resident in {time.time() - t0:.1f} s")
-
-    shape = sk.Shape(L, Hq, Hkv, d)
-    shape1 = sk.Shape(1, Hq, Hkv, d)
-    pol = sk.Policy(n, cfg.sinks, cfg.three_tier, cfg.budget)
-    plan = sk.plan_make(shape, pol)
-    lse = torch.empty((Hq, n), dtype=torch.float32, device=dev)
-    cws = torch.empty(max(1, sk.colsum_workspace_bytes(shape1, n)), dtype=torch.uint8, device=dev)
-    score = torch.empty(n, dtype=torch.float32, device=dev)
-    amap = torch.empty(n, dtype=torch.int32, device=dev)
-    order = torch.empty(n, dtype=torch.int32, device=dev)
-    payload = torch.empty(plan.payload_bytes, dtype=torch.uint8, device=dev)
-    Ko = torch.empty_like(K)
-    Vo = torch.empty_like(V)
-    bs = 16
-    nblk = (n + bs - 1) // bs
-    perm = np.random.default_rng(0).permutation(nblk).astype(np.int32)
-    block_table = torch.from_numpy(perm).to(dev)
-    Kc = torch.empty((L, nblk, bs, Hkv, d), dtype=torch.float16, device=dev)
-    Vc = torch.empty_like(Kc)
-
-    # practical bandwidth ceiling (and the counter calibration kernel of the
-    # traffic measurement): a device-to-device copy of the K+V bytes
-    src = K.view(-1).view(torch.uint8)
-    dst = torch.empty_like(src)
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    dst.copy_(src)
-    c0.record()
-    for _ in range(3):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 3 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del dst
-
-    stages = ["rowlse", "colsum", "assign", "pack", "unpack", "unpack_paged"]
-    ev = None
-    # pack and unpack are timed cold: a 1 GiB write before each of them
-    # evicts the 256 MB Infinity Cache (outside their events)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-
-    def evict():
-        scratch.fill_(0x5A)
-
-    def mark(name, i):
-        if ev is not None:
-            ev[name][i].record()
-
-    def step():
-        for layer in range(L):
-            mark("rowlse", 2 * layer)
-            sk.score_rowlse(shape1, Q[layer], K[layer], lse)
-            mark("rowlse", 2 * layer + 1)
-            mark("colsum", 2 * layer)
-            sk.score_colsum(shape1, Q[layer], K[layer], lse, score, layer > 0, cws)
-            mark("colsum", 2 * layer + 1)
-        mark("assign", 0)
-        sk.assign_tiers(pol, plan, score, amap, order)
-        mark("assign", 1)
-        evict()
-        mark("pack", 0)
-        sk.pack(shape, plan, K, V, amap, order, payload)
-        mark("pack", 1)
-        evict()
-        mark("unpack", 0)
-        sk.unpack(shape, plan, payload, amap, Ko, Vo)
-        mark("unpack", 1)
-        evict()
-        mark("unpack_paged", 0)
-        sk.unpack_paged(shape, plan, payload, amap, Kc, Vc, block_table, bs)
-        mark("unpack_paged", 1)
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    nev = {"rowlse": 2 * L, "colsum": 2 * L}
-    all_ev = [{s: [torch.cuda.Event(enable_timing=True) for _ in range(nev.get(s, 2))]
-               for s in stages} for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    wall0 = time.time()
-    start.record()
-    for i in range(args.steps):
-        ev = all_ev[i]
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.time() - wall0
-    ms_per_step = start.elapsed_time(end) / args.steps
-
-    # the score variants of the same request, timed on their own (they replace
-    # or reweight the score; they are not part of the step)
-    def timed(fn, reps):
+    def __call__(self, stage, work, fn):
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
+        a.record()
         fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for a, b in evs:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        b.record()
+        self.rec.append((stage, work, a, b))
 
-    alt = torch.empty(n, dtype=torch.float32, device=dev)
-    reps = max(3, args.steps)
-    t_kvnorm = timed(lambda: sk.score_kvnorm(shape, K, alt), reps) * 1e-3
-    t_recency = timed(lambda: sk.recency_weight(score, 1e-3, alt), reps) * 1e-3
+    def collect(self):
+        out = {}
+        for stage, work, a, b in self.rec:
+            ms, w = out.setdefault(stage, ([], []))
+            ms.append(a.elapsed_time(b))
+            w.append(work)
+        return {s: (np.array(ms), np.array(w, dtype=np.float64)) for s, (ms, w) in out.items()}
 
-    # cold-tier upgrade of n/8 seeded tokens: fp16 gather, then the paged scatter
-    n_up = n // 8
-    up_tokens = torch.from_numpy(
-        np.random.default_rng(1).choice(n, size=n_up, replace=False).astype(np.int32)).to(dev)
-    up_payload = torch.empty(sk.upgrade_bytes(shape, n_up), dtype=torch.uint8, device=dev)
-    t_up_pack = timed(lambda: sk.upgrade_pack(shape, K, V, up_tokens, up_payload), reps) * 1e-3
-    t_up_paged = timed(lambda: sk.upgrade_unpack_paged(shape, n, up_payload, up_tokens, Kc, Vc,
-                                                       block_table, bs), reps) * 1e-3
-    up_bytes = 2 * up_payload.numel() + 4 * n_up                 # rows read + written, list
 
-    # decode attention straight from the payload, all layers in one launch
-    # (one decode query per layer), and the same kernel over an all-fp16
-    # payload of the same request: the bytes a dense-KV attention reads
-    qdec = torch.from_numpy((np.random.default_rng(2).standard_normal((L, Hq, d)) * 0.5)
-                            .astype(np.float16)).to(dev)
-    odec = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
-    ldec = torch.empty((L, Hq), dtype=torch.float32, device=dev)
-    dws = torch.empty(max(1, sk.decode_workspace_bytes(shape, plan, L)), dtype=torch.uint8,
-                      device=dev)
-    t_dec = timed(lambda: sk.decode_attention(shape, plan, payload, qdec, odec, ldec, ws=dws),
-                  reps) * 1e-3
-    pol16 = sk.Policy(n, cfg.sinks, cfg.three_tier, 1.0)
-    plan16 = sk.plan_make(shape, pol16)
-    amap16 = torch.empty_like(amap)
-    order16 = torch.empty_like(order)
-    sk.assign_tiers(pol16, plan16, score, amap16, order16)
-    payload16 = torch.empty(plan16.payload_bytes, dtype=torch.uint8, device=dev)
-    sk.pack(shape, plan16, K, V, amap16, order16, payload16)
-    dws16 = torch.empty(max(1, sk.decode_workspace_bytes(shape, plan16, L)), dtype=torch.uint8,
-                        device=dev)
-    t_dec16 = timed(lambda: sk.decode_attention(shape, plan16, payload16, qdec, odec, ldec,
-                                                ws=dws16), reps) * 1e-3
-    del payload16
-    dec_io = L * Hq * d * (2 + 4) + L * Hq * 4                    # q in, out and lse written
-    dec_bytes = plan.payload_bytes + dec_io
-    dec16_bytes = plan16.payload_bytes + dec_io
-
-    # the score passes on one layer of each long-context workload's shape
-    # (seeded inputs of that workload): parity cases, not bench lines, timed
-    # here so the line shows the passes at their other head counts and d
-    score_shapes = {}
-    if not args.no_score_shapes:
-        for other in ("qwen25_7b_2tier", "gemma2_9b"):
-            oc = get_config(other)
-            ok_ = gen.keys(oc, 0)
-            oq = torch.from_numpy(gen.queries(oc, 0, k=ok_)).to(dev)
-            ok_ = torch.from_numpy(ok_).to(dev)
-            osh = sk.Shape(1, oc.q_heads, oc.kv_heads, oc.head_dim)
-            on = oc.tokens
-            olse = torch.empty((oc.q_heads, on), dtype=torch.float32, device=dev)
-            osc = torch.empty(on, dtype=torch.float32, device=dev)
-            ows = torch.empty(max(1, sk.colsum_workspace_bytes(osh, on)), dtype=torch.uint8,
-                              device=dev)
-            t_r = timed(lambda: sk.score_rowlse(osh, oq, ok_, olse), 3)
-            t_c = timed(lambda: sk.score_colsum(osh, oq, ok_, olse, osc, False, ows), 3)
-            f = oc.q_heads * oc.head_dim * on * (on + 1)
-            names = score_kernel_names(oc.q_heads, oc.kv_heads, oc.head_dim)
-            score_shapes[other] = {
-                "layer": f"Hq={oc.q_heads} Hkv={oc.kv_heads} d={oc.head_dim} n={on}",
-                "rowlse": {"kernel": names["rowlse"], "ms": round(t_r, 4),
-                           "tflops": round(f / (t_r * 1e-3) / 1e12, 1),
-                           "frac": round(f / (t_r * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
-                "colsum": {"kernel": names["colsum"], "ms": round(t_c, 4),
-                           "tflops": round(f / (t_c * 1e-3) / 1e12, 1),
-                           "frac": round(f / (t_c * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}}
-            del oq, ok_, olse, osc, ows
-            log(f"score passes on one {other} layer: {t_r:.3f} + {t_c:.3f} ms")
-
-    # per stage: [steps][launches] durations in ms
-    t = {s: np.array([[e[s][2 * j].elapsed_time(e[s][2 * j + 1]) for j in range(len(e[s]) // 2)]
-                      for e in all_ev]) for s in stages}
-    mean_launch = {s: float(t[s].mean()) for s in stages}          # ms per launch
-    per_step_ms = {s: float(t[s].sum(axis=1).mean()) for s in stages}
-    step_ms = {s: t[s].sum(axis=1) for s in stages}                # per timed step
-
-    kv_bytes = 2 * L * n * Hkv * d * 2
-    pack_bytes = kv_bytes + 4 * n + plan.payload_bytes                  # read K,V + map, write P
-    unpack_bytes = plan.payload_bytes + 4 * n + kv_bytes
-    t_pack = per_step_ms["pack"] * 1e-3
-    t_unpack = per_step_ms["unpack"] * 1e-3
-    t_paged = per_step_ms["unpack_paged"] * 1e-3
-    value = 2 * kv_bytes / (t_pack + t_unpack) / 1e9
-    pass_flops = Hq * d * n * (n + 1)                                   # one pass, one layer
-    score_s = (per_step_ms["rowlse"] + per_step_ms["colsum"]) * 1e-3
-    score_tflops = 2 * pass_flops * L / score_s / 1e12
-
-    dom = "colsum" if mean_launch["colsum"] >= mean_launch["rowlse"] else "rowlse"
-    ach = pass_flops / (mean_launch[dom] * 1e-3) / 1e12
-    kernel_name = score_kernel_names(Hq, Hkv, d)[dom]
-    nb = pack_batch(Hkv, d)
-
-    def rl(bytes_, sec, kernel):
-        gbs = bytes_ / sec / 1e9
-        return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": bytes_,
-                "traffic": counted_traffic(kernel, cfg.name)}
-
-    def call_rl(bytes_, sec):
-        gbs = bytes_ / sec / 1e9
-        return {"bound": "hbm", "call": "sk_decode_attention", "achieved": round(gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "bytes_per_call": bytes_}
-
-    line = {
-        "metric": "KV pack+unpack GB/s (fp16-equiv, % HBM peak); importance-score TFLOP/s",
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: L={L} Hq={Hq} Hkv={Hkv} d={d} n={n} S={cfg.sinks} "
-                               f"b={cfg.budget} {'3' if cfg.three_tier else '2'}-tier",
-                   "tokens": n, "layers": L, "budget": cfg.budget, "paged_block": bs},
-        "pack_unpack_pct_hbm": round((pack_bytes + unpack_bytes) / (t_pack + t_unpack) / 1e9
-                                     / HBM_PEAK_GBS, 4),
-        "score_tflops": round(score_tflops, 1),
-        "score_pct_mfma": round(score_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-        "stage_ms_per_step": {s: round(v, 4) for s, v in per_step_ms.items()},
-        "stage_ms_median": {s: round(float(np.median(v)), 4) for s, v in step_ms.items()},
-        "stage_ms_min": {s: round(float(v.min()), 4) for s, v in step_ms.items()},
-        "cold_cache": "1 GiB write before pack, unpack and paged unpack",
-        "payload_bytes": plan.payload_bytes,
-        "counts": {"fp16": plan.n16, "int8": plan.n8, "int4": plan.n4},
-        "roofline": {"bound": "mfma", "kernel": kernel_name, "achieved": round(ach, 1),
-                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": counted_traffic(kernel_name, cfg.name),
-                     "flops_per_launch": pass_flops,
-                     "avg_launch_ms": round(mean_launch[dom], 4)},
-        "roofline_stages": {"pack": rl(pack_bytes, t_pack, f"pack_kernel<{d},{nb}>"),
-                            "unpack": rl(unpack_bytes, t_unpack, f"unpack_kernel<{d},{nb},false>"),
-                            "unpack_paged": rl(unpack_bytes, t_paged,
-                                               f"unpack_kernel<{d},{nb},true>")},
-        "variants": {"kvnorm": rl(kv_bytes // 2 + 4 * n, t_kvnorm, f"kvnorm_kernel<{d}>"),
-                     # n = 8192 elements: one launch's latency, not a bandwidth figure
-                     "recency": {"bound": "latency", "kernel": "recency_kernel",
-                                 "us_per_launch": round(t_recency * 1e6, 2)}},
-        "upgrade": {"tokens": n_up,
-                    "pack": rl(up_bytes, t_up_pack, f"upgrade_pack_kernel<{d},{nb}>"),
-                    "unpack_paged": rl(up_bytes, t_up_paged,
-                                       f"upgrade_unpack_kernel<{d},{nb},true>")},
-        # whole sk_decode_attention calls (one partial launch per sent tier,
-        # then the merge): bytes and time of the call, not of one kernel
-        "decode": {"layers": L,
-                   "payload": call_rl(dec_bytes, t_dec),
-                   "fp16_payload": call_rl(dec16_bytes, t_dec16),
-                   "ms": round(t_dec * 1e3, 4), "fp16_ms": round(t_dec16 * 1e3, 4),
-                   "speedup_vs_fp16": round(t_dec16 / t_dec, 3)},
-        "score_other_shapes": score_shapes,
-        "copy_ceiling_gbs": round(copy_gbs, 1),
-        "copy_bytes": int(src.numel()),
-        "wall_s_timed": round(wall, 3),
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+def untimed(stage, work, fn):
+    fn()
 
 
 def score_kernel_names(Hq, Hkv, d):
@@ -372,7 +97,7 @@ def score_kernel_names(Hq, Hkv, d):
 
 
 def pack_batch(Hkv, d):
-    """Rows steps whose loads the pack/unpack kernels batch per token (the
+    """Row steps whose loads the pack/unpack kernels batch per token (the
     power of two, up to 8, covering 2*Hkv rows at 64/(d/8) rows a step)."""
     rpp = 64 // (d // 8)
     steps = (2 * Hkv + rpp - 1) // rpp
@@ -406,7 +131,414 @@ def counted_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(cfg, budget_s):
+def hbm_rl(bytes_, sec, kernel, workload, launches=1):
+    """Roofline entry of an HBM-bound kernel: algorithmic bytes per launch
+    over its average launch time."""
+    gbs = bytes_ / sec / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": int(round(bytes_ / launches)),
+            "avg_launch_ms": round(sec * 1e3 / launches, 4),
+            "traffic": counted_traffic(kernel, workload)}
+
+
+def mfma_rl(flops, ms, kernel, workload):
+    """Roofline entry of a score pass: causal single-pass QK^T flops per
+    launch (2 d per causal pair and query head) over its average launch
+    time, both averaged over the launches of the timed steps."""
+    ach = flops.sum() / (ms.sum() * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": kernel, "achieved": round(ach, 1),
+            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": counted_traffic(kernel, workload),
+            "flops_per_launch": float(flops.mean()), "avg_launch_ms": round(float(ms.mean()), 4),
+            "launches_per_step": None}
+
+
+def torch_copy_gbs(torch, nbytes, dev):
+    """torch's device-to-device copy of `nbytes` (r + w bytes / time): a
+    reference point, and the calibration kernel of the counter runs."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * 3 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+
+# --------------------------------------------------------------- batched mix --
+
+def run_batched(cfg, args, dev, torch, sk):
+    from workloads import gen, gen_device as gd
+
+    L, Hq, Hkv, d, bs = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.block_size
+    lengths = gen.request_lengths(cfg)
+    tables, num_blocks = gen.block_tables(cfg, lengths)
+    R = len(lengths)
+    nmax = max(lengths)
+    shape1 = sk.Shape(1, Hq, Hkv, d)
+    shape = sk.Shape(L, Hq, Hkv, d)
+    pols = {b: [sk.Policy(n, cfg.sinks, cfg.three_tier, b) for n in lengths] for b in cfg.budgets}
+    plans = {b: [sk.plan_make(shape, p) for p in pols[b]] for b in cfg.budgets}
+    kv = [2 * L * n * Hkv * d * 2 for n in lengths]
+    need = (sum(n * L * (Hq + 4 * Hkv) * d * 2 for n in lengths)
+            + sum(max(plans[b][r].payload_bytes for b in cfg.budgets) for r in range(R))
+            + (1 << 30))
+    free, total = torch.cuda.mem_get_info(dev)
+    log(f"batched mix: {R} requests, {sum(lengths)} tokens, lengths {lengths}; "
+        f"{need / 1e9:.1f} GB of device memory ({free / 1e9:.1f} GB free)")
+    if need > free:
+        raise SystemExit(f"the batched mix needs {need / 1e9:.1f} GB, {free / 1e9:.1f} GB free")
+
+    t0 = time.time()
+    Q, K, V = [], [], []
+    for r, n in enumerate(lengths):
+        Q.append(torch.empty((L, n, Hq, d), dtype=torch.float16, device=dev))
+        K.append(torch.empty((L, n, Hkv, d), dtype=torch.float16, device=dev))
+        V.append(torch.empty((L, n, Hkv, d), dtype=torch.float16, device=dev))
+        for layer in range(L):
+            gd.keys(cfg, layer, n, r, out=K[r][layer])
+            gd.values(cfg, layer, n, r, out=V[r][layer])
+            gd.queries(cfg, layer, n, r, k=K[r][layer], out=Q[r][layer])
+    torch.cuda.synchronize()
+    log(f"inputs resident in {time.time() - t0:.1f} s")
+
+    lse_all = torch.empty(Hq * nmax, dtype=torch.float32, device=dev)
+    cws = torch.empty(max(1, sk.colsum_workspace_bytes(shape1, nmax)), dtype=torch.uint8,
+                      device=dev)
+    lse = [lse_all[:Hq * n].view(Hq, n) for n in lengths]
+    score = [torch.empty(n, dtype=torch.float32, device=dev) for n in lengths]
+    amap = [torch.empty(n, dtype=torch.int32, device=dev) for n in lengths]
+    order = [torch.empty(n, dtype=torch.int32, device=dev) for n in lengths]
+    payload = [torch.empty(max(plans[b][r].payload_bytes for b in cfg.budgets),
+                           dtype=torch.uint8, device=dev) for r in range(R)]
+    btab = [torch.from_numpy(t).to(dev) for t in tables]
+    Kc = torch.empty((L, num_blocks, bs, Hkv, d), dtype=torch.float16, device=dev)
+    Vc = torch.empty_like(Kc)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    pass_flops = [Hq * d * n * (n + 1) for n in lengths]         # one pass, one layer
+
+    def pbytes(b, r):
+        n = lengths[r]
+        return kv[r] + 4 * n + plans[b][r].payload_bytes                     # K,V + map -> P
+
+    def ubytes(b, r):
+        n = lengths[r]
+        return plans[b][r].payload_bytes + 4 * n + 4 * len(tables[r]) + kv[r]  # P + map + bt -> KV
+
+    def step(m):
+        for r in range(R):
+            for layer in range(L):
+                m("rowlse", pass_flops[r],
+                  lambda: sk.score_rowlse(shape1, Q[r][layer], K[r][layer], lse[r]))
+                m("colsum", pass_flops[r],
+                  lambda: sk.score_colsum(shape1, Q[r][layer], K[r][layer], lse[r], score[r],
+                                          layer > 0, cws))
+        for b in cfg.budgets:
+            for r in range(R):
+                m(f"assign@{b}", 0,
+                  lambda: sk.assign_tiers(pols[b][r], plans[b][r], score[r], amap[r], order[r]))
+            scratch.fill_(0x5A)      # evict the Infinity Cache before the pack phase
+            for r in range(R):
+                m(f"pack@{b}", pbytes(b, r),
+                  lambda: sk.pack(shape, plans[b][r], K[r], V[r], amap[r], order[r],
+                                  payload[r][:plans[b][r].payload_bytes]))
+            scratch.fill_(0x5A)
+            for r in range(R):
+                m(f"unpack_paged@{b}", ubytes(b, r),
+                  lambda: sk.unpack_paged(shape, plans[b][r],
+                                          payload[r][:plans[b][r].payload_bytes], amap[r],
+                                          Kc, Vc, btab[r], bs))
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(untimed)
+    torch.cuda.synchronize()
+    marks = [Marks(torch) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    wall0 = time.time()
+    start.record()
+    for i in range(args.steps):
+        step(marks[i])
+        log(f"step {i + 1} enqueued")
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    res = [m.collect() for m in marks]
+
+    def cat(stage):
+        return (np.concatenate([r_[stage][0] for r_ in res]),
+                np.concatenate([r_[stage][1] for r_ in res]))
+
+    K_ = args.steps
+    t_pack = sum(cat(f"pack@{b}")[0].sum() for b in cfg.budgets) * 1e-3 / K_
+    t_unp = sum(cat(f"unpack_paged@{b}")[0].sum() for b in cfg.budgets) * 1e-3 / K_
+    kv_total = sum(kv)
+    nb_ = len(cfg.budgets)
+    value = 2 * kv_total * nb_ / (t_pack + t_unp) / 1e9
+    moved = sum(pbytes(b, r) + ubytes(b, r) for b in cfg.budgets for r in range(R))
+    rms, rfl = cat("rowlse")
+    cms, cfl = cat("colsum")
+    score_s = (rms.sum() + cms.sum()) * 1e-3 / K_
+    score_flops = 2 * L * sum(pass_flops)
+    score_tflops = score_flops / score_s / 1e12
+    names = score_kernel_names(Hq, Hkv, d)
+    dom = "colsum" if cms.sum() >= rms.sum() else "rowlse"
+    roof = mfma_rl(*((cfl, cms) if dom == "colsum" else (rfl, rms)), names[dom], cfg.name)
+    roof["launches_per_step"] = R * L
+    nbk = pack_batch(Hkv, d)
+
+    per_budget = {}
+    for b in cfg.budgets:
+        pm, _ = cat(f"pack@{b}")
+        um, _ = cat(f"unpack_paged@{b}")
+        am, _ = cat(f"assign@{b}")
+        tp, tu = pm.sum() * 1e-3 / K_, um.sum() * 1e-3 / K_
+        pb = sum(pbytes(b, r) for r in range(R))
+        ub = sum(ubytes(b, r) for r in range(R))
+        per_budget[str(b)] = {
+            "payload_bytes": sum(plans[b][r].payload_bytes for r in range(R)),
+            "counts": [int(sum(getattr(plans[b][r], f) for r in range(R)))
+                       for f in ("n16", "n8", "n4")],
+            "fp16_equiv_gbs": round(2 * kv_total / (tp + tu) / 1e9, 1),
+            "pack": hbm_rl(pb, tp, f"pack_kernel<{d},{nbk}>", cfg.name, R),
+            "unpack_paged": hbm_rl(ub, tu, f"unpack_kernel<{d},{nbk},true>", cfg.name, R),
+            "assign_ms_per_step": round(am.sum() / K_, 4)}
+
+    # score efficiency per request (launches of all layers and steps)
+    per_req = []
+    nrl = len(rms) // K_ // R            # = L
+    for r, n in enumerate(lengths):
+        idx = np.concatenate([np.arange(s * R * nrl + r * nrl, s * R * nrl + (r + 1) * nrl)
+                              for s in range(K_)])
+        f = pass_flops[r] * len(idx)
+        per_req.append({"n": n, "rowlse_ms": round(float(rms[idx].mean()), 4),
+                        "colsum_ms": round(float(cms[idx].mean()), 4),
+                        "rowlse_frac": round(f / (rms[idx].sum() * 1e-3) / 1e12
+                                             / MFMA_F16_PEAK_TFLOPS, 4),
+                        "colsum_frac": round(f / (cms[idx].sum() * 1e-3) / 1e12
+                                             / MFMA_F16_PEAK_TFLOPS, 4)})
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": f"{cfg.name}: {R} requests of Mistral-7B shape (L={L} Hq={Hq} "
+                               f"Hkv={Hkv} d={d}), lengths log-uniform in [{cfg.len_lo}, "
+                               f"{cfg.len_hi}] ({sum(lengths)} tokens), S={cfg.sinks}, 3-tier, "
+                               f"b in {list(cfg.budgets)}, paged unpack ({bs}-token blocks)",
+                   "requests": R, "tokens": sum(lengths), "lengths": lengths, "layers": L,
+                   "budgets": list(cfg.budgets), "paged_block": bs,
+                   "kv_fp16_bytes": kv_total},
+        "pack_unpack_pct_hbm": round(moved / (t_pack + t_unp) / 1e9 / HBM_PEAK_GBS, 4),
+        "score_tflops": round(score_tflops, 1),
+        "score_pct_mfma": round(score_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "score_flops_per_step": float(score_flops),
+        "roofline": roof,
+        "roofline_other_pass": mfma_rl(*((rfl, rms) if dom == "colsum" else (cfl, cms)),
+                                       names["rowlse" if dom == "colsum" else "colsum"],
+                                       cfg.name),
+        "stage_ms_per_step": {"rowlse": round(rms.sum() / K_, 3),
+                              "colsum": round(cms.sum() / K_, 3),
+                              "pack": round(t_pack * 1e3, 3),
+                              "unpack_paged": round(t_unp * 1e3, 3)},
+        "budgets": per_budget,
+        "score_per_request": per_req,
+        "cold_cache": "1 GiB write before each pack phase and each unpack phase",
+        "wall_s_timed": round(wall, 3),
+    }
+    del Q, K, V, Kc, Vc, payload, scratch, lse_all, cws
+    return line, lengths
+
+
+# ----------------------------------------------------------- single request --
+
+def run_single(cfg, steps, warmup, dev, torch, sk, extras):
+    from workloads import gen_device as gd
+
+    L, Hq, Hkv, d, n = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.tokens
+    log(f"workload {cfg.name}: L={L} Hq={Hq} Hkv={Hkv} d={d} n={n}")
+    t0 = time.time()
+    Q = torch.empty((L, n, Hq, d), dtype=torch.float16, device=dev)
+    K = torch.empty((L, n, Hkv, d), dtype=torch.float16, device=dev)
+    V = torch.empty((L, n, Hkv, d), dtype=torch.float16, device=dev)
+    for layer in range(L):
+        gd.keys(cfg, layer, n, out=K[layer])
+        gd.values(cfg, layer, n, out=V[layer])
+        gd.queries(cfg, layer, n, k=K[layer], out=Q[layer])
+    torch.cuda.synchronize()
+    log(f"inputs resident in {time.time() - t0:.1f} s")
+
+    shape = sk.Shape(L, Hq, Hkv, d)
+    shape1 = sk.Shape(1, Hq, Hkv, d)
+    pol = sk.Policy(n, cfg.sinks, cfg.three_tier, cfg.budget)
+    plan = sk.plan_make(shape, pol)
+    lse = torch.empty((Hq, n), dtype=torch.float32, device=dev)
+    cws = torch.empty(max(1, sk.colsum_workspace_bytes(shape1, n)), dtype=torch.uint8, device=dev)
+    score = torch.empty(n, dtype=torch.float32, device=dev)
+    amap = torch.empty(n, dtype=torch.int32, device=dev)
+    order = torch.empty(n, dtype=torch.int32, device=dev)
+    payload = torch.empty(plan.payload_bytes, dtype=torch.uint8, device=dev)
+    Ko = torch.empty_like(K)
+    Vo = torch.empty_like(V)
+    bs = 16
+    nblk = (n + bs - 1) // bs
+    block_table = torch.from_numpy(
+        np.random.default_rng(0).permutation(nblk).astype(np.int32)).to(dev)
+    Kc = torch.empty((L, nblk, bs, Hkv, d), dtype=torch.float16, device=dev)
+    Vc = torch.empty_like(Kc)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    kv_bytes = 2 * L * n * Hkv * d * 2
+    pass_flops = Hq * d * n * (n + 1)
+    pack_bytes = kv_bytes + 4 * n + plan.payload_bytes
+    unpack_bytes = plan.payload_bytes + 4 * n + kv_bytes
+    paged_bytes = unpack_bytes + 4 * nblk
+
+    def step(m):
+        for layer in range(L):
+            m("rowlse", pass_flops, lambda: sk.score_rowlse(shape1, Q[layer], K[layer], lse))
+            m("colsum", pass_flops, lambda: sk.score_colsum(shape1, Q[layer], K[layer], lse,
+                                                            score, layer > 0, cws))
+        m("assign", 0, lambda: sk.assign_tiers(pol, plan, score, amap, order))
+        scratch.fill_(0x5A)
+        m("pack", pack_bytes, lambda: sk.pack(shape, plan, K, V, amap, order, payload))
+        scratch.fill_(0x5A)
+        m("unpack", unpack_bytes, lambda: sk.unpack(shape, plan, payload, amap, Ko, Vo))
+        scratch.fill_(0x5A)
+        m("unpack_paged", paged_bytes,
+          lambda: sk.unpack_paged(shape, plan, payload, amap, Kc, Vc, block_table, bs))
+
+    for _ in range(warmup):
+        step(untimed)
+    torch.cuda.synchronize()
+    marks = [Marks(torch) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(marks[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+    res = [m.collect() for m in marks]
+
+    def cat(stage):
+        return (np.concatenate([r_[stage][0] for r_ in res]),
+                np.concatenate([r_[stage][1] for r_ in res]))
+
+    per = {s: cat(s)[0].sum() * 1e-3 / steps for s in
+           ("rowlse", "colsum", "assign", "pack", "unpack", "unpack_paged")}
+    rms, rfl = cat("rowlse")
+    cms, cfl = cat("colsum")
+    names = score_kernel_names(Hq, Hkv, d)
+    dom = "colsum" if cms.sum() >= rms.sum() else "rowlse"
+    score_tflops = 2 * L * pass_flops / (per["rowlse"] + per["colsum"]) / 1e12
+    nbk = pack_batch(Hkv, d)
+    out = {
+        "config": {"workload": f"{cfg.name}: L={L} Hq={Hq} Hkv={Hkv} d={d} n={n} S={cfg.sinks} "
+                               f"b={cfg.budget} {'3' if cfg.three_tier else '2'}-tier",
+                   "tokens": n, "layers": L, "budget": cfg.budget, "paged_block": bs},
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 3),
+        "value": round(2 * kv_bytes / (per["pack"] + per["unpack"]) / 1e9, 1),
+        "unit": "GB/s (fp16-equiv pack + dense unpack)",
+        "pack_unpack_pct_hbm": round((pack_bytes + unpack_bytes) / (per["pack"] + per["unpack"])
+                                     / 1e9 / HBM_PEAK_GBS, 4),
+        "score_tflops": round(score_tflops, 1),
+        "score_pct_mfma": round(score_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "roofline": dict(mfma_rl(*((cfl, cms) if dom == "colsum" else (rfl, rms)), names[dom],
+                                 cfg.name), launches_per_step=L),
+        "roofline_other_pass": dict(mfma_rl(*((rfl, rms) if dom == "colsum" else (cfl, cms)),
+                                            names["rowlse" if dom == "colsum" else "colsum"],
+                                            cfg.name), launches_per_step=L),
+        "roofline_stages": {
+            "pack": hbm_rl(pack_bytes, per["pack"], f"pack_kernel<{d},{nbk}>", cfg.name),
+            "unpack": hbm_rl(unpack_bytes, per["unpack"], f"unpack_kernel<{d},{nbk},false>",
+                             cfg.name),
+            "unpack_paged": hbm_rl(paged_bytes, per["unpack_paged"],
+                                   f"unpack_kernel<{d},{nbk},true>", cfg.name)},
+        "stage_ms_per_step": {s: round(v * 1e3, 4) for s, v in per.items()},
+        "payload_bytes": plan.payload_bytes,
+        "counts": {"fp16": plan.n16, "int8": plan.n8, "int4": plan.n4},
+        "cold_cache": "1 GiB write before pack, unpack and paged unpack",
+    }
+
+    def timed(fn, reps):
+        fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+    reps = 5
+    # decode attention straight from the payload, all layers in one call (one
+    # decode query per layer): whole calls, one partial launch per sent tier
+    # plus the merge; the per-kernel times are in the rocprofv3 summaries
+    qdec = torch.from_numpy((np.random.default_rng(2).standard_normal((L, Hq, d)) * 0.5)
+                            .astype(np.float16)).to(dev)
+    odec = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
+    ldec = torch.empty((L, Hq), dtype=torch.float32, device=dev)
+    dws = torch.empty(max(1, sk.decode_workspace_bytes(shape, plan, L)), dtype=torch.uint8,
+                      device=dev)
+    t_dec = timed(lambda: sk.decode_attention(shape, plan, payload, qdec, odec, ldec, ws=dws),
+                  reps)
+    dec_bytes = plan.payload_bytes + L * Hq * d * (2 + 4) + L * Hq * 4
+    out["decode"] = {"layers": L, "call": "sk_decode_attention",
+                     "achieved": round(dec_bytes / t_dec / 1e9, 1), "unit": "GB/s",
+                     "frac": round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes_per_call": dec_bytes, "ms": round(t_dec * 1e3, 4)}
+    if extras:
+        alt = torch.empty(n, dtype=torch.float32, device=dev)
+        t_kvnorm = timed(lambda: sk.score_kvnorm(shape, K, alt), reps)
+        t_recency = timed(lambda: sk.recency_weight(score, 1e-3, alt), reps)
+        n_up = n // 8
+        up_tokens = torch.from_numpy(
+            np.random.default_rng(1).choice(n, size=n_up, replace=False).astype(np.int32)).to(dev)
+        up_payload = torch.empty(sk.upgrade_bytes(shape, n_up), dtype=torch.uint8, device=dev)
+        t_up_pack = timed(lambda: sk.upgrade_pack(shape, K, V, up_tokens, up_payload), reps)
+        t_up_paged = timed(lambda: sk.upgrade_unpack_paged(shape, n, up_payload, up_tokens, Kc,
+                                                           Vc, block_table, bs), reps)
+        up_bytes = 2 * up_payload.numel() + 4 * n_up
+        out["variants"] = {"kvnorm": hbm_rl(kv_bytes // 2 + 4 * n, t_kvnorm,
+                                            f"kvnorm_kernel<{d}>", cfg.name),
+                           "recency": {"bound": "latency", "kernel": "recency_kernel",
+                                       "us_per_launch": round(t_recency * 1e6, 2)}}
+        out["upgrade"] = {"tokens": n_up,
+                          "pack": hbm_rl(up_bytes, t_up_pack, f"upgrade_pack_kernel<{d},{nbk}>",
+                                         cfg.name),
+                          "unpack_paged": hbm_rl(up_bytes, t_up_paged,
+                                                 f"upgrade_unpack_kernel<{d},{nbk},true>",
+                                                 cfg.name)}
+        out["torch_copy_gbs"] = round(torch_copy_gbs(torch, 512 << 20, dev), 1)
+    del Q, K, V, Ko, Vo, Kc, Vc, payload, scratch
+    return out
+
+
+# ------------------------------------------------------------- CPU baseline --
+
+def cpu_baseline(cfg, lengths, budget_s):
     """The oracle, as it stands, timed on the host cores on a bounded sample of
     the same workload; reported in the metric's unit."""
     from oracle import assign as OA, plan as OP, quant as OQ, score as OS
@@ -418,31 +550,40 @@ def cpu_baseline(cfg, budget_s):
     except Exception:  # pragma: no cover
         blas = None
     cores = len(os.sched_getaffinity(0))
-    L, Hq, Hkv, d, n = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.tokens
-    opl = OP.make_plan(L, Hq, Hkv, d, n, cfg.sinks, cfg.budget, cfg.three_tier)
-    # pack + unpack of whole layers until about half the budget is spent
-    k = gen.keys(cfg, 0)
-    v = gen.values(cfg, 0)
+    L, Hq, Hkv, d = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim
+    if lengths:
+        r = int(np.argmin([abs(n - 8192) for n in lengths]))   # a mid-length request
+        n, b = lengths[r], 0.5
+    else:
+        r, n, b = 0, cfg.tokens, cfg.budget
+    opl = OP.make_plan(L, Hq, Hkv, d, n, cfg.sinks, b, cfg.three_tier)
+    k = gen.keys(cfg, 0, n, request=r)
+    v = gen.values(cfg, 0, n, request=r)
     s32 = np.random.default_rng(0).random(n).astype(np.float32)
     t0 = time.time()
     _, _, amap, _ = OA.assign(s32, opl.n16, opl.n8, opl.n4, opl.sinks)
     t_assign = time.time() - t0
-    layers = 0
-    t_pu = 0.0
+    layers, t_pu = 0, 0.0
     buf = np.zeros(opl.payload_bytes, dtype=np.uint8)
+    bs = cfg.block_size
+    nblk = (n + bs - 1) // bs
+    bt = np.arange(nblk, dtype=np.int32)
+    kc = np.zeros((1, nblk, bs, Hkv, d), dtype=np.float16)
+    vc = np.zeros_like(kc)
     while t_pu < budget_s / 2 and layers < L:
         t0 = time.time()
         for off, data in OQ.pack_layer(k, v, layers, amap, opl):
             buf[off:off + data.size] = data
-        OQ.unpack_layer(buf, layers, amap, opl, Hkv, d)
+        kk, vv = OQ.unpack_layer(buf, layers, amap, opl, Hkv, d)
+        j = np.arange(n)
+        kc[0, bt[j // bs], j % bs] = kk
+        vc[0, bt[j // bs], j % bs] = vv
         t_pu += time.time() - t0
         layers += 1
     kv_layer = 2 * n * Hkv * d * 2
     gbs = 2 * kv_layer * layers / t_pu / 1e9
-    # score: whole (layer, head) pairs in fp64 until the other half is spent
-    q = gen.queries(cfg, 0, k=k)
-    heads = 0
-    t_sc = 0.0
+    q = gen.queries(cfg, 0, n, request=r, k=k)
+    heads, t_sc = 0, 0.0
     while t_sc < budget_s / 2 and heads < Hq:
         t0 = time.time()
         OS.head_column_sums(q[:, heads, :], k[:, heads // (Hq // Hkv), :])
@@ -451,9 +592,52 @@ def cpu_baseline(cfg, budget_s):
     tflops = heads * d * n * (n + 1) / t_sc / 1e12          # single-pass QK^T count
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "blas_threads": blas,
             "kind": "oracle",
-            "sample": f"pack+unpack of {layers} of {L} layers (fp16-equiv GB/s, numpy, "
-                      f"1 thread); score of {heads} (layer, head) pairs of {L * Hq} in fp64",
-            "score_tflops": round(tflops, 6), "assign_s_full": round(t_assign, 3)}
+            "sample": f"request {r} (n={n}) of {cfg.name}: pack+unpack of {layers} of {L} "
+                      f"layers at b={b} (fp16-equiv GB/s, numpy, 1 thread); score of {heads} "
+                      f"(layer, head) pairs of {L * Hq} in fp64 (BLAS threads)",
+            "score_tflops": round(tflops, 6), "assign_s_one_request": round(t_assign, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the transfer path is built and timed on a "
+              "single MI355X (multi-GPU sharding is a design note, not a measured path).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import serving_sk_score_amd as sk
+    from workloads import get_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sk.lib()  # fails loudly if the HIP library is not built
+    dev = torch.device("cuda", 0)
+    cfg = get_config(args.workload)
+    if cfg.requests:
+        line, lengths = run_batched(cfg, args, dev, torch, sk)
+    else:
+        one = run_single(cfg, args.steps, args.warmup, dev, torch, sk, extras=True)
+        lengths = None
+        line = {"metric": METRIC, "value": one.pop("value"), "unit": "GB/s", "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "ms_per_step": one.pop("ms_per_step"),
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "f16", "data": "synthetic (seeded, drawn on the device)", **one}
+    gc.collect()
+    torch.cuda.empty_cache()
+    others = [w for w in args.others.split(",") if w and w != cfg.name]
+    if others:
+        line["workloads"] = {}
+        for w in others:
+            line["workloads"][w] = run_single(get_config(w), args.other_steps, 1, dev, torch, sk,
+                                              extras=(w == "mistral7b"))
+            gc.collect()
+            torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, lengths, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
