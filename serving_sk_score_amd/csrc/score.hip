@@ -239,7 +239,13 @@ __global__ __launch_bounds__(W * QW * 64, D == 256 ? 1 : 2) void rowlse_kernel(
     constexpr int C = D / 16;
     constexpr int PITCH = D + 8;
     constexpr int U = KS / 32;  // 32-key units per stage
-    extern __shared__ _Float16 smem[];  // [2][KS][PITCH]
+    constexpr int SB = KS * PITCH;  // halfs per stage buffer
+    // a ring of three stage buffers [3][KS][PITCH]: stage s lives in buffer
+    // s % 3 and is stored at the end of stage s - 2, before that stage's
+    // barrier, so during stage s the next stage's buffer is already valid
+    // (its first fragments are read ahead) and the buffer written at the end
+    // of stage s (that of s + 2, last read in stage s - 1) is free
+    extern __shared__ _Float16 smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -277,25 +283,30 @@ __global__ __launch_bounds__(W * QW * 64, D == 256 ? 1 : 2) void rowlse_kernel(
     const _Float16* Kg = K + (int64_t)g * D;
     const int64_t kstride = (int64_t)Hkv * D;
     auto kload = [&](int s) { st.load(Kg + key0(s) * kstride, n - key0(s), kstride); };
+    // prologue: stages 0 and 1 in LDS, stage 2 in flight
     st.init(tid, kstride);
     kload(0);
     st.store(smem);
-    if (ns > 1) kload(1);
+    if (ns > 1) {
+        kload(1);
+        st.store(smem + SB);
+        if (ns > 2) kload(2);
+    }
     __syncthreads();
 
     float m[2] = {-INFINITY, -INFINITY};
     float s[2] = {0.0f, 0.0f};
     auto next_stage = [&](int si) {
-        if (si + 1 < ns) {
-            st.store(smem + ((si + 1) & 1) * (KS * PITCH));
-            if (si + 2 < ns) kload(si + 2);
+        if (si + 2 < ns) {
+            st.store(smem + ((si + 2) % 3) * SB);
+            if (si + 3 < ns) kload(si + 3);
         }
         __syncthreads();
     };
 
     // diagonal stages: causal mask, exact online max
     for (int si = 0; si < nd; ++si) {
-        const _Float16* buf = smem + (si & 1) * (KS * PITCH);
+        const _Float16* buf = smem + (si % 3) * SB;
         const int64_t k0 = key0(si);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -328,25 +339,41 @@ __global__ __launch_bounds__(W * QW * 64, D == 256 ? 1 : 2) void rowlse_kernel(
 
     // stages strictly below the diagonal: no mask, fixed reference.  The
     // pipeline runs the softmax of each 32-key unit while the MFMAs of the
-    // next unit (in this stage or the next) execute; `pend` starts as -inf,
-    // which contributes exactly zero.
+    // next unit (in this stage or the next) execute, and each key fragment is
+    // read from LDS two MFMA steps before its use (the first two of a unit
+    // during the previous unit, across a stage boundary too); `pend` starts
+    // as -inf, which contributes exactly zero.
     floatx16 pend[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         pend[0][e] = -INFINITY;
         pend[1][e] = -INFINITY;
     }
+    const int fo = col * PITCH + khalf;  // this lane's fragment offset in a unit
+    half8 pf[2];                         // the next unit's first two fragments
+    if (nd < ns) {
+        pf[0] = *reinterpret_cast<const half8*>(smem + (nd % 3) * SB + fo);
+        pf[1] = *reinterpret_cast<const half8*>(smem + (nd % 3) * SB + fo + 16);
+    }
     for (int si = nd; si < ns; ++si) {
-        const _Float16* buf = smem + (si & 1) * (KS * PITCH);
+        const _Float16* buf = smem + (si % 3) * SB;
+        const _Float16* nbuf = smem + ((si + 1) % 3) * SB;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const _Float16* urow = buf + 32 * u * PITCH + fo;
+            const _Float16* nrow = (u + 1 < U) ? urow + 32 * PITCH : nbuf + fo;
+            half8 f[C];
+            f[0] = pf[0];
+            f[1] = pf[1];
             floatx16 cur0 = zero16(), cur1 = zero16();
-            const _Float16* arow = buf + (32 * u + col) * PITCH + khalf;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                const half8 a = *reinterpret_cast<const half8*>(arow + c * 16);
-                cur0 = mfma32(a, qf[0][c], cur0);
-                cur1 = mfma32(a, qf[1][c], cur1);
+                if (c + 2 < C)
+                    f[c + 2] = *reinterpret_cast<const half8*>(urow + (c + 2) * 16);
+                else
+                    pf[c + 2 - C] = *reinterpret_cast<const half8*>(nrow + (c + 2 - C) * 16);
+                cur0 = mfma32(f[c], qf[0][c], cur0);
+                cur1 = mfma32(f[c], qf[1][c], cur1);
             }
             fixed_ref_update(pend, c2, lane, m, s);
             pend[0] = cur0;
@@ -402,11 +429,16 @@ __global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
     constexpr int C = D / 16;
     constexpr int PITCH = D + 8;
     constexpr int U = QS / 32;  // 32-query units per stage
+    constexpr int SB = QS * PITCH;  // halfs per stage buffer
     static_assert(QS <= NT, "one lse value per thread and stage");
-    // [2][QS][PITCH] query tiles, then float [3][QS] lse values: the pipeline
-    // reads a stage's lse values one stage after its query tile
+    // a ring of three stage buffers [3][QS][PITCH] of query tiles, then float
+    // [3][QS] lse values.  Stage s lives in buffer s % 3 and is stored at the
+    // end of stage s - 2, before that stage's barrier, so during stage s the
+    // buffer of stage s + 1 is already valid (the next stage's first
+    // fragments are read ahead) and the buffer written at the end of stage s
+    // (that of s + 2, last read in stage s - 1) is no longer read by anyone.
     extern __shared__ _Float16 smem[];
-    float* lsm = reinterpret_cast<float*>(smem + 2 * QS * PITCH);
+    float* lsm = reinterpret_cast<float*>(smem + 3 * SB);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -417,7 +449,7 @@ __global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
     const int64_t K0 = (int64_t)blockIdx.y * (kColKeys * KW);  // blockIdx.y = 0: most work
     const int64_t k0 = K0 + kColKeys * wave;
 
-    // stationary key fragments (B operand of S = Q K^T)
+    // stationary key fragments (A operand of S^T = K Q^T)
     half8 kf[2][C];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -442,6 +474,7 @@ __global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
         const int64_t t0 = K0 + (int64_t)QS * s;
         st.load(Qh + t0 * qstride, n - t0, qstride);
     };
+    // prologue: stages 0 and 1 in LDS, stage 2 in flight
     st.init(tid, qstride);
     qload(0);
     float lv = lload(0);
@@ -450,6 +483,12 @@ __global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
     if (ns > 1) {
         qload(1);
         lv = lload(1);
+        st.store(smem + SB);
+        if (tid < QS) lsm[QS + tid] = lv;
+        if (ns > 2) {
+            qload(2);
+            lv = lload(2);
+        }
     }
     __syncthreads();
 
@@ -461,43 +500,79 @@ __global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
         for (int e = 0; e < 16; ++e) ca[t][e] = 0.0f;
     // Software pipeline over the stages after this wavefront's keys: the
     // weights of each 32-query unit are summed while the MFMAs of the next
-    // unit execute.  `pend` starts as -inf with a finite or +inf lse, which
+    // unit execute, and each fragment is read from LDS one MFMA step before
+    // its use (the first one of a unit during the previous unit, across a
+    // stage boundary too).  `pend` starts as -inf with lse 0, which
     // contributes exactly zero.  At d = 256 the MFMAs of a unit take twice
     // its softmax time and the 32 registers of the pending tiles would leave
     // one wavefront per SIMD, so there each unit is summed right after its
     // own MFMAs and the two wavefronts of a SIMD overlap each other instead.
     constexpr bool kPipe = D != 256;
     floatx16 pend[2];
-    const float* pL = lsm;  // lse values of the pending unit (the first stage's)
+    // lse of the pending unit's query: read from LDS when the unit's MFMAs
+    // are issued, so the softmax one unit later waits on no LDS read
+    float pL = 0.0f;
+    // fragments are read one MFMA step ahead (two steps measured the same and
+    // need two more registers than the 256 a wavefront has here)
+    constexpr int kPf = 1;
+    half8 pf[kPf];  // the next unit's first fragment, read ahead
+    bool have_pf = false;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         pend[0][e] = -INFINITY;
         pend[1][e] = -INFINITY;
     }
     for (int si = 0; si < ns; ++si) {
-        const _Float16* buf = smem + (si & 1) * (QS * PITCH);
+        const _Float16* buf = smem + (si % 3) * SB;
+        const _Float16* nbuf = smem + ((si + 1) % 3) * SB;
         const float* lb = lsm + (si % 3) * QS;
         const int64_t s0 = K0 + (int64_t)QS * si;
         if (s0 >= k0 + kColKeys) {
             // every query of the stage is after every key of this wavefront
+            if constexpr (kPipe) {
+                const int fo = col * PITCH + khalf;  // this lane's fragment offset in a unit
+                if (!have_pf) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                floatx16 cur0 = zero16(), cur1 = zero16();
-                const _Float16* brow = buf + (32 * u + col) * PITCH + khalf;
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    const half8 b = *reinterpret_cast<const half8*>(brow + c * 16);
-                    cur0 = mfma32(kf[0][c], b, cur0);
-                    cur1 = mfma32(kf[1][c], b, cur1);
+                    for (int c = 0; c < kPf; ++c)
+                        pf[c] = *reinterpret_cast<const half8*>(buf + fo + c * 16);
                 }
-                if constexpr (kPipe) {
-                    const float L = pL[col];
-                    tile_colacc(pend[0], L, c2, ca[0]);
-                    tile_colacc(pend[1], L, c2, ca[1]);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const _Float16* urow = buf + 32 * u * PITCH + fo;
+                    const _Float16* nrow = (u + 1 < U) ? urow + 32 * PITCH : nbuf + fo;
+                    half8 f[C];
+#pragma unroll
+                    for (int c = 0; c < kPf; ++c) f[c] = pf[c];
+                    floatx16 cur0 = zero16(), cur1 = zero16();
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        if (c + kPf < C)
+                            f[c + kPf] = *reinterpret_cast<const half8*>(urow + (c + kPf) * 16);
+                        else
+                            pf[c + kPf - C] =
+                                *reinterpret_cast<const half8*>(nrow + (c + kPf - C) * 16);
+                        cur0 = mfma32(kf[0][c], f[c], cur0);
+                        cur1 = mfma32(kf[1][c], f[c], cur1);
+                    }
+                    const float Lnext = lb[32 * u + col];
+                    tile_colacc(pend[0], pL, c2, ca[0]);
+                    tile_colacc(pend[1], pL, c2, ca[1]);
                     pend[0] = cur0;
                     pend[1] = cur1;
-                    pL = lb + 32 * u;
-                } else {
+                    pL = Lnext;
+                }
+                have_pf = true;
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    floatx16 cur0 = zero16(), cur1 = zero16();
+                    const _Float16* brow = buf + (32 * u + col) * PITCH + khalf;
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        const half8 b = *reinterpret_cast<const half8*>(brow + c * 16);
+                        cur0 = mfma32(kf[0][c], b, cur0);
+                        cur1 = mfma32(kf[1][c], b, cur1);
+                    }
                     const float L = lb[32 * u + col];
                     tile_colacc(cur0, L, c2, ca[0]);
                     tile_colacc(cur1, L, c2, ca[1]);
@@ -526,20 +601,19 @@ __global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
                 if (need1) tile_colacc_masked(acc1, L, c2, last - 32, lane, ca[1]);
             }
         }
-        if (si + 1 < ns) {
-            st.store(smem + ((si + 1) & 1) * (QS * PITCH));
-            if (tid < QS) lsm[((si + 1) % 3) * QS + tid] = lv;
-            if (si + 2 < ns) {
-                qload(si + 2);
-                lv = lload(si + 2);
+        if (si + 2 < ns) {
+            st.store(smem + ((si + 2) % 3) * SB);
+            if (tid < QS) lsm[((si + 2) % 3) * QS + tid] = lv;
+            if (si + 3 < ns) {
+                qload(si + 3);
+                lv = lload(si + 3);
             }
         }
         __syncthreads();
     }
     if constexpr (kPipe) {
-        const float L = pL[col];
-        tile_colacc(pend[0], L, c2, ca[0]);
-        tile_colacc(pend[1], L, c2, ca[1]);
+        tile_colacc(pend[0], pL, c2, ca[0]);
+        tile_colacc(pend[1], pL, c2, ca[1]);
     }
     // sum each key row over the 32 query lanes of its half by a transpose
     // reduction: at the exchange with lane ^ m (m = 16, 8, 4, 2) a lane keeps
@@ -620,7 +694,7 @@ hipError_t launch_rowlse_t(const Dims& s, const void* q, const void* k, float* l
     const int64_t QB = 64 * QW;
     const dim3 grid((unsigned)(s.Hq / W), (unsigned)((s.n + QB - 1) / QB));
     const float c2 = kLog2e / sqrtf((float)s.d);
-    const size_t lds = (size_t)2 * KS * (D + 8) * 2;
+    const size_t lds = (size_t)3 * KS * (D + 8) * 2;
     hipLaunchKernelGGL((rowlse_kernel<D, W, QW, KS>), grid, dim3(W * QW * 64), lds, st,
                        (const _Float16*)q, (const _Float16*)k, lse2, s.n, s.Hq, s.Hkv, c2);
     return hipGetLastError();
@@ -644,7 +718,7 @@ hipError_t launch_colsum_d(const Dims& s, const void* q, const void* k, const fl
     const int64_t KB = (int64_t)kColKeys * kColWaves;
     const dim3 grid((unsigned)s.Hq, (unsigned)((s.n + KB - 1) / KB));
     const float c2 = kLog2e / sqrtf((float)s.d);
-    const size_t lds = (size_t)2 * QS * (D + 8) * 2 + (size_t)3 * QS * 4;
+    const size_t lds = (size_t)3 * QS * (D + 8) * 2 + (size_t)3 * QS * 4;
     hipLaunchKernelGGL((colsum_kernel<D, kColWaves, QS>), grid, dim3(kColWaves * 64), lds, st,
                        (const _Float16*)q, (const _Float16*)k, lse2, partial, s.n,
                        padded_tokens(s.n), s.Hq, s.Hkv, c2);
