@@ -78,5 +78,73 @@ def build(verbose=False, jobs=4):
     return LIB
 
 
+# Host-sanitized build: the same sources and device code, with the host C++
+# (argument validation, the plan's closed form, workspace sizes, launch-grid
+# arithmetic) instrumented by AddressSanitizer and UndefinedBehaviorSanitizer.
+# Every sanitizer flag applies to the host pass only.  The result is a test
+# artefact under _build/, loaded into a process that preloads the ASan
+# runtime (asan_runtime()); it is never the library the package loads.
+SAN_DIR = os.path.join(OBJDIR, "host_san")
+SAN_LIB = os.path.join(SAN_DIR, "libsk_host_san.so")
+_SAN = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+        "-fno-omit-frame-pointer", "-g"]
+
+
+def _host_only(flags):
+    out = []
+    for f in flags:
+        out += ["-Xarch_host", f]
+    return out
+
+
+def build_host_sanitized(verbose=False, jobs=6):
+    """Build (when a source is newer than the last build) and return the path
+    of the host-sanitized library."""
+    srcs = [os.path.join(CSRC, f) for f in SOURCES + ["sk_kernels.h"]]
+    srcs.append(os.path.join(INCLUDE, "sk.h"))
+    if os.path.exists(SAN_LIB) and os.path.getmtime(SAN_LIB) >= max(map(os.path.getmtime, srcs)):
+        return SAN_LIB
+    os.makedirs(SAN_DIR, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(SAN_DIR, src + ".o")
+        cmd = [hipcc(), *FLAGS, *_host_only(_SAN), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src} (host-sanitized):\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max(1, jobs)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           *_host_only(["-fsanitize=address", "-fsanitize=undefined", "-shared-libsan"]),
+           *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (host-sanitized):\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def asan_runtime():
+    """The shared ASan runtime of the ROCm compiler (preloaded into the
+    process that loads the host-sanitized library)."""
+    for clang in ("/opt/rocm/llvm/bin/clang", shutil.which("clang")):
+        if not clang or not os.path.exists(clang):
+            continue
+        r = subprocess.run([clang, "-print-resource-dir"], capture_output=True, text=True)
+        if r.returncode == 0:
+            path = os.path.join(r.stdout.strip(), "lib", "linux", "libclang_rt.asan-x86_64.so")
+            if os.path.exists(path):
+                return path
+    raise RuntimeError("ASan runtime of the ROCm compiler not found")
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

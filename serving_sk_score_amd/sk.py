@@ -101,40 +101,46 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is not built; run `python -m serving_sk_score_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        P = ctypes.POINTER
-        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        sig = {
-            "sk_plan_make": (i32, [P(_Shape), P(_Policy), P(_Plan)]),
-            "sk_score_workspace_bytes": (sz, [P(_Shape), i64]),
-            "sk_score": (i32, [P(_Shape), i64, vp, vp, vp, i32, vp, sz, vp]),
-            "sk_score_noalloc": (i32, [P(_Shape), i64, vp, vp, vp, i32, vp]),
-            "sk_score_rowlse": (i32, [P(_Shape), i64, vp, vp, vp, vp]),
-            "sk_score_colsum_workspace_bytes": (sz, [P(_Shape), i64]),
-            "sk_score_colsum": (i32, [P(_Shape), i64, vp, vp, vp, vp, i32, vp, sz, vp]),
-            "sk_assign_workspace_bytes": (sz, [i64]),
-            "sk_assign_tiers": (i32, [P(_Policy), P(_Plan), vp, vp, vp, vp, sz, vp]),
-            "sk_pack": (i32, [P(_Shape), P(_Plan), vp, vp, vp, vp, vp, vp]),
-            "sk_unpack": (i32, [P(_Shape), P(_Plan), vp, vp, vp, vp, P(_Paged), vp]),
-            "sk_status_string": (ctypes.c_char_p, [i32]),
-            "sk_last_error": (ctypes.c_char_p, []),
-            "sk_layout_version": (i32, []),
-            "sk_recency_weight": (i32, [i64, ctypes.c_double, vp, vp, vp]),
-            "sk_score_kvnorm": (i32, [P(_Shape), i64, vp, vp, i32, vp]),
-            "sk_upgrade_bytes": (sz, [P(_Shape), i64]),
-            "sk_balanced_keys": (i32, [i64, i32, vp, vp]),
-            "sk_decode_workspace_bytes": (sz, [P(_Shape), P(_Plan), i32]),
-            "sk_decode_attention": (i32, [P(_Shape), P(_Plan), vp, i32, i32, vp, vp, vp, vp, sz,
-                                          vp]),
-            "sk_upgrade_pack": (i32, [P(_Shape), i64, vp, vp, vp, i64, vp, vp]),
-            "sk_upgrade_unpack": (i32, [P(_Shape), i64, vp, vp, i64, vp, vp, P(_Paged), vp]),
-        }
-        for name, (res, args) in sig.items():
-            f = getattr(L, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = L
+        _lib = bind(LIB_PATH)
     return _lib
+
+
+def bind(path):
+    """Load a build of the C ABI at `path` and declare the signatures of its
+    entry points (lib() binds the in-tree libsk.so this way)."""
+    L = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "sk_plan_make": (i32, [P(_Shape), P(_Policy), P(_Plan)]),
+        "sk_score_workspace_bytes": (sz, [P(_Shape), i64]),
+        "sk_score": (i32, [P(_Shape), i64, vp, vp, vp, i32, vp, sz, vp]),
+        "sk_score_noalloc": (i32, [P(_Shape), i64, vp, vp, vp, i32, vp]),
+        "sk_score_rowlse": (i32, [P(_Shape), i64, vp, vp, vp, vp]),
+        "sk_score_colsum_workspace_bytes": (sz, [P(_Shape), i64]),
+        "sk_score_colsum": (i32, [P(_Shape), i64, vp, vp, vp, vp, i32, vp, sz, vp]),
+        "sk_assign_workspace_bytes": (sz, [i64]),
+        "sk_assign_tiers": (i32, [P(_Policy), P(_Plan), vp, vp, vp, vp, sz, vp]),
+        "sk_pack": (i32, [P(_Shape), P(_Plan), vp, vp, vp, vp, vp, vp]),
+        "sk_unpack": (i32, [P(_Shape), P(_Plan), vp, vp, vp, vp, P(_Paged), vp]),
+        "sk_status_string": (ctypes.c_char_p, [i32]),
+        "sk_last_error": (ctypes.c_char_p, []),
+        "sk_layout_version": (i32, []),
+        "sk_recency_weight": (i32, [i64, ctypes.c_double, vp, vp, vp]),
+        "sk_score_kvnorm": (i32, [P(_Shape), i64, vp, vp, i32, vp]),
+        "sk_upgrade_bytes": (sz, [P(_Shape), i64]),
+        "sk_balanced_keys": (i32, [i64, i32, vp, vp]),
+        "sk_decode_workspace_bytes": (sz, [P(_Shape), P(_Plan), i32]),
+        "sk_decode_attention": (i32, [P(_Shape), P(_Plan), vp, i32, i32, vp, vp, vp, vp, sz,
+                                      vp]),
+        "sk_upgrade_pack": (i32, [P(_Shape), i64, vp, vp, vp, i64, vp, vp]),
+        "sk_upgrade_unpack": (i32, [P(_Shape), i64, vp, vp, i64, vp, vp, P(_Paged), vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
 
 
 def _check(status):

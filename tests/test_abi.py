@@ -16,6 +16,12 @@ import serving_sk_score_amd.sk as sk
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sk.h")
 
+# tests/test_host_sanitize.py runs this module in a child process whose
+# SK_ABI_TEST_LIB names a host-sanitized build of the same sources; every
+# call below then goes through that build.
+if os.environ.get("SK_ABI_TEST_LIB"):
+    sk._lib = sk.bind(os.environ["SK_ABI_TEST_LIB"])
+
 
 def _declared():
     text = open(HEADER).read()
