@@ -1,0 +1,76 @@
+"""Every column of the importance score at the longest lengths the workloads
+have, against the fp64 oracle (SpectrumKV §4.3 "Importance scores",
+Algorithm 1 "score tokens"): one KV group of a layer, so that all n
+columns - the sink and early columns, whose sums run over tens of thousands
+of query rows, as well as the late ones - are checked element by element at
+the 2e-3 relative tolerance.
+
+The score is additive over (layer, KV group) and the kernels compute each
+group independently, so the group's query heads and its one KV head are
+passed as a layer of their own (H_q = the group size, H_kv = 1).  That keeps
+the grouping ratio, and with it the row pass's heads per workgroup and every
+workgroup's work, exactly as in the full layer; the column sums are then the
+oracle's layer score restricted to those heads.  The oracle runs one head
+per thread (numpy releases the interpreter lock inside BLAS and ufuncs)."""
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import score as OS
+import serving_sk_score_amd as sk
+from workloads import gen, get_config
+from tests.gpu_helpers import Guarded, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 2e-3
+
+
+def _group_check(name, q, k, g, tag):
+    n, Hq, d = q.shape
+    R = Hq // k.shape[1]
+    qg = np.ascontiguousarray(q[:, g * R:(g + 1) * R, :])
+    kg = np.ascontiguousarray(k[:, g:g + 1, :])
+    shape = sk.Shape(1, R, 1, d)
+    out = Guarded(4 * n)
+    say(f"{tag}: GPU score of KV group {g} ({R} heads), n={n}, d={d}")
+    sk.score(shape, to_dev(qg), to_dev(kg), out.as_(torch.float32, (n,)), False)
+    torch.cuda.synchronize()
+    out.check()
+    got = out.as_(torch.float32, (n,)).cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)) and np.all(got > 0)
+    assert abs(got.sum() - R * n) <= 1e-4 * R * n, "row-stochastic invariant"
+    say(f"{tag}: oracle (fp64), {R} heads on {R} threads ...")
+    with ThreadPoolExecutor(R) as ex:
+        parts = list(ex.map(lambda h: OS.head_column_sums(qg[:, h, :], kg[:, 0, :]), range(R)))
+    want = np.sum(parts, axis=0)
+    rel = np.abs(got - want) / want
+    worst = int(np.argmax(rel))
+    say(f"{tag}: max rel err {rel.max():.3g} at column {worst}; columns 0-63 max "
+        f"{rel[:64].max():.3g}")
+    assert rel.max() <= RTOL, (f"{tag}: column {worst}: {got[worst]} vs {want[worst]} "
+                               f"(rel {rel[worst]:.3g})")
+
+
+@pytest.mark.parametrize("name,layer,g", [("qwen25_7b_2tier", 0, 0), ("gemma2_9b", 0, 0)])
+def test_every_column_one_group(name, layer, g):
+    cfg = get_config(name)
+    k = gen.keys(cfg, layer)
+    q = gen.queries(cfg, layer, k=k)
+    _group_check(name, q, k, g, f"{name} layer {layer}")
+
+
+def test_every_column_longest_batched_request():
+    """The 64,226-token request of the batched mix (Mistral-7B shape, 4 query
+    heads per KV head), on the layer the batched test samples for it."""
+    cfg = get_config("batched_mix")
+    lengths = gen.request_lengths(cfg)
+    r = int(np.argmax(lengths))
+    n = lengths[r]
+    layer = r % cfg.layers
+    k = gen.keys(cfg, layer, n, request=r)
+    q = gen.queries(cfg, layer, n, request=r, k=k)
+    _group_check("batched_mix", q, k, 0, f"batched request {r} (n={n}) layer {layer}")
