@@ -311,8 +311,8 @@ def run_batched(cfg, args, dev, torch, sk):
             "counts": [int(sum(getattr(plans[b][r], f) for r in range(R)))
                        for f in ("n16", "n8", "n4")],
             "fp16_equiv_gbs": round(2 * kv_total / (tp + tu) / 1e9, 1),
-            "pack": hbm_rl(pb, tp, f"pack_kernel<{d},{nbk}>", cfg.name, R),
-            "unpack_paged": hbm_rl(ub, tu, f"unpack_kernel<{d},{nbk},true>", cfg.name, R),
+            "pack": hbm_rl(pb, tp, f"pack_kernel<{d},{nbk}>", f"{cfg.name}@{b}", R),
+            "unpack_paged": hbm_rl(ub, tu, f"unpack_kernel<{d},{nbk},true>", f"{cfg.name}@{b}", R),
             "assign_ms_per_step": round(am.sum() / K_, 4)}
 
     # score efficiency per request (launches of all layers and steps)
