@@ -165,7 +165,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
     constexpr int LPT = CP < 64 ? CP : 64;        // lanes per token group in p.V
     constexpr int TG = 64 / LPT;                  // token groups (2 for d = 64)
     constexpr int DWL = CP / LPT;                 // pairs owned per lane in p.V
-    constexpr int PITCH = lds_pitch<D>();         // vt: [64 tokens][PITCH] dwords
+    constexpr int PITCH = lds_pitch<D>();         // vt: [64 tokens (32 at d = 256)][PITCH] dwords
+    constexpr bool kSplitV = D == 256;            // V through LDS one block at a time
     static_assert(GM <= 32, "query group wider than the MFMA tile");
     // pp: [32 token pairs][GM heads] fp16 probability pairs
 
@@ -220,34 +221,41 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
         for (int i = 0; i < NPH; ++i) asm volatile("" : "+v"(R.k[i]), "+v"(R.v[i]));
         if constexpr (TIER != 0) asm volatile("" : "+v"(R.sk), "+v"(R.sv));
     };
-    // dequantize a block: K into the S^T MFMAs, V into its LDS rows (rows of
-    // slots past the tier's end hold a copy of its last token; their
-    // probabilities are exactly 0)
-    auto process_block = [&](const BlockRegs<NPH>& R, int blk, f16v& c) {
-        h2 sk2 = {(_Float16)1.0f, (_Float16)1.0f}, sv2 = sk2;
+    // dequantize a block's K into the S^T MFMAs, one 16-byte piece at a time
+    // (each piece's fp16 pairs feed their MFMAs right away, so the whole
+    // dequantized half row is never held)
+    auto k_block = [&](const BlockRegs<NPH>& R, f16v& c) {
+        h2 sk2 = {(_Float16)1.0f, (_Float16)1.0f};
         if constexpr (TIER != 0) {
             // consumed here, not earlier: a wait for a prefetched block's
             // scale would also wait for every load issued before it
-            uint32_t ks = R.sk, vs = R.sv;
-            asm volatile("" : "+v"(ks), "+v"(vs));
+            uint32_t ks = R.sk;
+            asm volatile("" : "+v"(ks));
             sk2 = as_h2(ks | (ks << 16));
-            sv2 = as_h2(vs | (vs << 16));
         }
-        uint32_t kpairs[HP];
+        c = f16v{};
 #pragma unroll
         for (int i = 0; i < NPH; ++i) {
             uint32_t pr[TI::PPP];
             piece_pairs<D, TIER>(R.k[i], sk2, pr);
 #pragma unroll
-            for (int e = 0; e < TI::PPP; ++e) kpairs[i * TI::PPP + e] = pr[e];
+            for (int j = 0; j < TI::PPP / 4; ++j)
+                c = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    pairs_h8(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]),
+                    qb[i * (TI::PPP / 4) + j], c, 0, 0, 0);
         }
-        c = f16v{};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                pairs_h8(kpairs[4 * kk], kpairs[4 * kk + 1], kpairs[4 * kk + 2], kpairs[4 * kk + 3]),
-                qb[kk], c, 0, 0, 0);
-        uint32_t* vrow = &vt[(32 * blk + r) * PITCH + hb * HP];
+    };
+    // dequantize a block's V into the LDS rows (rows of slots past the
+    // tier's end hold a copy of its last token; their probabilities are
+    // exactly 0)
+    auto v_block = [&](const BlockRegs<NPH>& R, int row0) {
+        h2 sv2 = {(_Float16)1.0f, (_Float16)1.0f};
+        if constexpr (TIER != 0) {
+            uint32_t vs = R.sv;
+            asm volatile("" : "+v"(vs));
+            sv2 = as_h2(vs | (vs << 16));
+        }
+        uint32_t* vrow = &vt[(row0 + r) * PITCH + hb * HP];
 #pragma unroll
         for (int i = 0; i < NPH; ++i) {
             uint32_t pv[TI::PPP];
@@ -267,26 +275,69 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
         for (int k = 0; k < DWL; ++k) o[h][k][0] = o[h][k][1] = 0.0f;
 
     BlockRegs<NPH> A, B;
+    // p.V of token pairs [tp0, tp0 + NTP) of the tile, whose V rows are in
+    // LDS from row vr0 on: lanes own channel pairs, tokens two at a time
+    auto pv_rows = [&](auto ntp, int tp0, int vr0) {
+        constexpr int NTP = decltype(ntp)::value;
+        const int tg = TG > 1 ? lane / LPT : 0;
+        const int wl = TG > 1 ? lane % LPT : lane;
+#pragma unroll
+        for (int it = 0; it < NTP / TG; ++it) {
+            const int tp = it * TG + tg;          // token pair within the rows
+            uint32_t pw[GM];
+#pragma unroll
+            for (int h = 0; h < GM; ++h) pw[h] = pp[(tp0 + tp) * GM + h];
+#pragma unroll
+            for (int k = 0; k < DWL; ++k) {
+                const int w = wl + k * LPT;
+                const uint32_t x = vt[(vr0 + 2 * tp) * PITCH + w];
+                const uint32_t y = vt[(vr0 + 2 * tp + 1) * PITCH + w];
+                const h2 a0 = as_h2(__builtin_amdgcn_perm(y, x, 0x05040100u));
+                const h2 a1 = as_h2(__builtin_amdgcn_perm(y, x, 0x07060302u));
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+                    o[h][k][0] = __builtin_amdgcn_fdot2(a0, as_h2(pw[h]), o[h][k][0], false);
+                    o[h][k][1] = __builtin_amdgcn_fdot2(a1, as_h2(pw[h]), o[h][k][1], false);
+                }
+            }
+        }
+    };
     // one 64-token tile: blocks s0 and s0 + 32 (A holds the first, already
-    // loaded); the next tile's first block is loaded while this one is used
-    // (the prefetch is a compile-time choice: a load issued on one branch only
-    // would make the wait counts of the merged paths conservative)
-    // Holding the next block while using this one doubles the load registers;
-    // measured, it pays even where it leaves one wave per SIMD (8 pieces per
-    // half row: fp16 at d = 128, int8 at d = 256).  fp16 rows at d = 256 (16
-    // pieces) would spill: there both blocks of a tile are loaded at its start.
-    constexpr bool PREF = NPH <= 8;
+    // loaded, when the next tile's first block is prefetched).
+    //  - d <= 128: each block's K runs through the MFMAs and its V into its
+    //    32 rows of the 64-row LDS tile; the next tile's first block is
+    //    loaded into A as soon as A is used (holding it doubles the load
+    //    registers; measured, it pays even where it leaves one wave per SIMD,
+    //    8 pieces per half row: fp16 at d = 128).
+    //  - d = 256 (kSplitV): both blocks' K run through the MFMAs, then each
+    //    block's V goes through one 32-row LDS tile in turn, and both blocks
+    //    are loaded at the tile's start (no prefetch).  Halving the LDS tile
+    //    and the load registers lets two wavefronts share a SIMD: the
+    //    Gemma-shaped call went from 42% to 48.6% of the HBM peak, while at
+    //    d = 128 this order was 1-3% slower than the one above.
+    // (The prefetch is a compile-time choice: a load issued on one branch
+    // only would make the wait counts of the merged paths conservative.)
+    constexpr bool PREF = !kSplitV && NPH <= 8;
     auto tile_body = [&](auto masked, auto prefetch, int64_t s0) {
         constexpr bool MASKED = decltype(masked)::value;
         constexpr bool PREFETCH = PREF && decltype(prefetch)::value;
         f16v c[2];
-        if constexpr (!PREF) load_block(A, s0);
-        load_block(B, s0 + 32);
-        if constexpr (PREF) pin(A);
-        process_block(A, 0, c[0]);
-        if constexpr (PREFETCH) load_block(A, s0 + 64);
-        if constexpr (PREF) pin(B);
-        process_block(B, 1, c[1]);
+        if constexpr (kSplitV) {
+            load_block(A, s0);
+            load_block(B, s0 + 32);
+            k_block(A, c[0]);
+            k_block(B, c[1]);
+        } else {
+            if constexpr (!PREF) load_block(A, s0);
+            load_block(B, s0 + 32);
+            if constexpr (PREF) pin(A);
+            k_block(A, c[0]);
+            v_block(A, 0);
+            if constexpr (PREFETCH) load_block(A, s0 + 64);
+            if constexpr (PREF) pin(B);
+            k_block(B, c[1]);
+            v_block(B, 32);
+        }
 
         // S^T fragment: lane holds head r, tokens 32*blk + 8*(e/4) + 4*hb + e%4
         if constexpr (MASKED) {
@@ -336,30 +387,19 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
                 o[h][k][1] *= al;
             }
         }
-        __syncthreads();
-
-        // p.V: lanes own channel pairs, tokens two at a time
-        const int tg = TG > 1 ? lane / LPT : 0;
-        const int wl = TG > 1 ? lane % LPT : lane;
-#pragma unroll
-        for (int it = 0; it < 32 / TG; ++it) {
-            const int tp = it * TG + tg;
-            uint32_t pw[GM];
-#pragma unroll
-            for (int h = 0; h < GM; ++h) pw[h] = pp[tp * GM + h];
-#pragma unroll
-            for (int k = 0; k < DWL; ++k) {
-                const int w = wl + k * LPT;
-                const uint32_t x = vt[(2 * tp) * PITCH + w];
-                const uint32_t y = vt[(2 * tp + 1) * PITCH + w];
-                const h2 a0 = as_h2(__builtin_amdgcn_perm(y, x, 0x05040100u));
-                const h2 a1 = as_h2(__builtin_amdgcn_perm(y, x, 0x07060302u));
-#pragma unroll
-                for (int h = 0; h < GM; ++h) {
-                    o[h][k][0] = __builtin_amdgcn_fdot2(a0, as_h2(pw[h]), o[h][k][0], false);
-                    o[h][k][1] = __builtin_amdgcn_fdot2(a1, as_h2(pw[h]), o[h][k][1], false);
-                }
-            }
+        using p16 = std::integral_constant<int, 16>;
+        using p32 = std::integral_constant<int, 32>;
+        if constexpr (kSplitV) {
+            v_block(A, 0);
+            __syncthreads();
+            pv_rows(p16{}, 0, 0);
+            __syncthreads();
+            v_block(B, 0);
+            __syncthreads();
+            pv_rows(p16{}, 16, 0);
+        } else {
+            __syncthreads();
+            pv_rows(p32{}, 0, 0);
         }
         __syncthreads();
     };
@@ -417,7 +457,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
 // registers for their union): blockIdx.x is the chunk within the tier.
 template <int D, int TIER, int GM>
 __global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
-    __shared__ uint32_t vt[64 * lds_pitch<D>()];
+    __shared__ uint32_t vt[(D == 256 ? 32 : 64) * lds_pitch<D>()];
     __shared__ uint32_t pp[32 * GM];
     partial_body<D, TIER, GM>(a, a.tier[TIER], blockIdx.x, vt, pp);
 }
