@@ -268,7 +268,9 @@ sk_status sk_assign_tiers(const sk_policy* policy, const sk_plan* plan,
  *   s = fp16_rne(fl32(max|x| / qmax)),  qmax = 127 / 7,
  *   q = clamp(rint_even(fl32(x / s)), -qmax, qmax)   (q = 0 when s == 0),
  * written at the row's slot in the layout described at sk_plan.
- *   k, v    : fp16 [n_layers][n][n_kv_heads][head_dim]
+ *   k, v    : fp16 [n_layers][n][n_kv_heads][head_dim], finite (a NaN or
+ *             Inf in an int8 / int4 row leaves that row's codes and scale
+ *             unspecified; every write stays in bounds)
  *   map     : from sk_assign_tiers (entries whose slot is out of range for
  *             their tier are skipped)
  *   order   : from sk_assign_tiers (may be NULL; reserved for layouts that

@@ -13,8 +13,8 @@
 // of a row.  The tier is uniform across the wave, so there is no divergence
 // between the fp16 copy and the int8/int4 paths.
 //
-// Exact arithmetic: the scale needs one correctly rounded fp32 division per
-// row (a / qmax) and one for r = 1/s.  Each element then uses
+// Exact arithmetic without a divider: the scale needs fl32(a / qmax) and
+// r = fl32(1 / s) per row (see quant8), and each element then uses
 //   q0 = x*r,  e = fma(-q0, s, x),  q1 = fma(e, r, q0)
 // which equals the correctly rounded quotient fl32(x/s) for every pair of
 // fp16 x and fp16 s with |x/s| <= 300 (Markstein's correction step; checked
@@ -58,34 +58,64 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 // Quantize 8 elements of one row whose absmax over the whole row is `a`.
+// The row's scale needs fl32(a / QMAX) and fl32(1 / s); neither uses the
+// divider: a / QMAX is a multiply by fl32(1 / QMAX) and one fused correction,
+// and 1 / s one Newton step from the hardware reciprocal (within one ulp of
+// 1 / s); both equal the correctly rounded quotients for every fp16 a and s
+// (checked exhaustively on the CPU).  Each code is clamped to [-QMAX, QMAX]
+// and rounded to nearest even by adding 1.5 * 2^23, the float whose unit is
+// 1 in [2^23, 2^24): the result's low bits then hold the code in two's
+// complement (its low byte is the int8 code, its low nibble the int4 one).
+// Clamping before rounding gives the same code as after, the bounds being
+// integers.
 template <int QMAX>
-__device__ __forceinline__ void quant8(const float (&x)[8], float a, int (&q)[8],
+__device__ __forceinline__ void quant8(const float (&x)[8], float a, uint32_t (&cb)[8],
                                        uint32_t& sbits) {
-    const float s32 = a / (float)QMAX;  // IEEE division
+    constexpr float kRq = 1.0f / (float)QMAX;
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    const float d0 = a * kRq;
+    const float s32 = fmaf(fmaf(-d0, (float)QMAX, a), kRq, d0);
     const __half s16 = __float2half_rn(s32);
     sbits = __half_as_ushort(s16);
     const float s = __half2float(s16);
     if (s == 0.0f) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = 0;
+        for (int e = 0; e < 8; ++e) cb[e] = 0u;
         return;
     }
-    const float r = 1.0f / s;  // IEEE division
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float r = fmaf(fmaf(-r0, s, 1.0f), r0, r0);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float q0 = x[e] * r;
         const float err = fmaf(-q0, s, x[e]);
         const float q1 = fmaf(err, r, q0);
-        float t = rintf(q1);
-        t = fminf(fmaxf(t, -(float)QMAX), (float)QMAX);
-        q[e] = (int)t;
+        const float c = __builtin_amdgcn_fmed3f(q1, -(float)QMAX, (float)QMAX);
+        cb[e] = __float_as_uint(c + kMagic);
     }
+}
+
+// The low bytes of four code words as one dword (element e in byte e).
+__device__ __forceinline__ uint32_t bytes4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+    const uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0C0C0400u);   // [c0, c1, 0, 0]
+    const uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x04000C0Cu);   // [0, 0, c2, c3]
+    return lo | hi;
+}
+
+// Eight int4 codes (low nibbles of the code words) as one dword, element 2m
+// in bits 0-3 and element 2m+1 in bits 4-7 of byte m.
+__device__ __forceinline__ uint32_t nibbles8(const uint32_t (&cb)[8]) {
+    uint32_t b0 = bytes4(cb[0], cb[1], cb[2], cb[3]) & 0x0F0F0F0Fu;
+    uint32_t b1 = bytes4(cb[4], cb[5], cb[6], cb[7]) & 0x0F0F0F0Fu;
+    b0 |= b0 >> 4;  // byte 0: e0 | e1 << 4, byte 2: e2 | e3 << 4
+    b1 |= b1 >> 4;
+    return __builtin_amdgcn_perm(b1, b0, 0x06040200u);
 }
 
 // One lane's 8 elements of a row (a 16-byte piece of fp16) quantized against
 // the absmax of the whole row, taken over the row's LPR lanes.
 template <int QMAX, int LPR>
-__device__ __forceinline__ void quant_piece(const uint4 raw, int (&q)[8], uint32_t& sbits) {
+__device__ __forceinline__ void quant_piece(const uint4 raw, uint32_t (&q)[8], uint32_t& sbits) {
     float x[8];
     x[0] = h2f(raw.x);
     x[1] = h2f(raw.x >> 16);
@@ -187,14 +217,12 @@ __global__ __launch_bounds__(kWaves * 64) void pack_kernel(
             for (int i = 0; i < NB; ++i) {
                 const int r = b0 + i * RPP + lane / LPR;
                 if (b0 + i * RPP < rows) {  // whole steps: the row group's lanes together
-                    int q[8];
+                    uint32_t q[8];
                     uint32_t sbits;
                     quant_piece<127, LPR>(raw[i], q, sbits);
                     uint2 w;
-                    w.x = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) |
-                          ((uint32_t)(q[3] & 0xFF) << 24);
-                    w.y = (q[4] & 0xFF) | ((q[5] & 0xFF) << 8) | ((q[6] & 0xFF) << 16) |
-                          ((uint32_t)(q[7] & 0xFF) << 24);
+                    w.x = bytes4(q[0], q[1], q[2], q[3]);
+                    w.y = bytes4(q[4], q[5], q[6], q[7]);
                     if (r < rows) {
                         const int64_t row = rowbase + r;
                         st_nt(w, out + sg.oc[1] + row * D + part * 8);
@@ -209,12 +237,10 @@ __global__ __launch_bounds__(kWaves * 64) void pack_kernel(
             for (int i = 0; i < NB; ++i) {
                 const int r = b0 + i * RPP + lane / LPR;
                 if (b0 + i * RPP < rows) {
-                    int q[8];
+                    uint32_t q[8];
                     uint32_t sbits;
                     quant_piece<7, LPR>(raw[i], q, sbits);
-                    uint32_t w = 0;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) w |= (uint32_t)(q[e] & 0xF) << (4 * e);
+                    const uint32_t w = nibbles8(q);
                     if (r < rows) {
                         const int64_t row = rowbase + r;
                         st_nt(w, out + sg.oc[2] + row * (D / 2) + part * 4);

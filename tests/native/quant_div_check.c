@@ -14,8 +14,12 @@
  * Plain C, IEEE binary32 arithmetic (build with -ffp-contract=off and
  * without -ffast-math so that every operation is rounded exactly once as
  * written; fmaf is the C library's correctly rounded fused multiply-add).
- * Prints "pairs=<checked> mismatches=<m>" and the first mismatches; exits
- * 1 on any mismatch (2 if its own fp16 decoding fails its fixed points).
+ * It also checks the two divisions that fix the row's scale (see the end of
+ * main): fl32(a / qmax) by a multiply and one fused correction, and
+ * fl32(1 / s) by one Newton step from any approximation within one ulp.
+ * Prints "pairs=<checked> mismatches=<m> scale_checks=<c> scale_mismatches=<m>"
+ * and the first mismatches; exits 1 on any mismatch (2 if its own fp16
+ * decoding fails its fixed points).
  * Built with -DDROP_CORRECTION it checks q0 instead of q1, a planted mistake
  * the tests use to show that the check can fail. */
 #include <math.h>
@@ -92,6 +96,55 @@ int main(void) {
             }
         }
     }
-    printf("pairs=%lld mismatches=%lld\n", pairs, mismatches);
-    return mismatches ? 1 : 0;
+    /* The scale's two divisions, done without a divider:
+     * (a) s32 = fl32(a / qmax): with rq = fl32(1 / qmax),
+     *     q0 = fl32(a * rq), e = fma(-q0, qmax, a), s32 = fma(e, rq, q0),
+     *     for every finite fp16 a >= 0 and qmax in {7, 127};
+     * (b) r = fl32(1 / s) from any first approximation r0 within one ulp of
+     *     it (the hardware reciprocal's bound): e = fma(-r0, s, 1),
+     *     r = fma(e, r0, r0), for every positive finite fp16 s and each r0 in
+     *     {fl32(1/s) - 1 ulp, fl32(1/s), fl32(1/s) + 1 ulp}. */
+    long long scale_checks = 0, scale_mismatches = 0;
+    const float qmaxes[2] = {7.0f, 127.0f};
+    for (int qi = 0; qi < 2; ++qi) {
+        const float qm = qmaxes[qi];
+        const float rq = 1.0f / qm;
+        for (uint32_t h = 0; h < 0x7C00; ++h) {
+            const float a = val[h];
+            const float q0 = a * rq;
+#ifdef DROP_CORRECTION
+            const float s32 = q0;
+#else
+            const float e = fmaf(-q0, qm, a);
+            const float s32 = fmaf(e, rq, q0);
+#endif
+            ++scale_checks;
+            if (bits_of(s32) != bits_of(a / qm)) {
+                if (++scale_mismatches <= 5)
+                    printf("scale mismatch: a=%a qmax=%g got %a want %a\n", a, qm, s32, a / qm);
+            }
+        }
+    }
+    for (uint32_t h = 1; h < 0x7C00; ++h) {
+        const float s = val[h];
+        const float rn = 1.0f / s;
+        const float cand[3] = {nextafterf(rn, 0.0f), rn, nextafterf(rn, INFINITY)};
+        for (int c = 0; c < 3; ++c) {
+            const float r0 = cand[c];
+#ifdef DROP_CORRECTION
+            const float r = r0;
+#else
+            const float e = fmaf(-r0, s, 1.0f);
+            const float r = fmaf(e, r0, r0);
+#endif
+            ++scale_checks;
+            if (bits_of(r) != bits_of(rn)) {
+                if (++scale_mismatches <= 5)
+                    printf("reciprocal mismatch: s=%a r0=%a got %a want %a\n", s, r0, r, rn);
+            }
+        }
+    }
+    printf("pairs=%lld mismatches=%lld scale_checks=%lld scale_mismatches=%lld\n", pairs,
+           mismatches, scale_checks, scale_mismatches);
+    return (mismatches || scale_mismatches) ? 1 : 0;
 }

@@ -146,3 +146,61 @@ def test_full_size_sampled_layers(name):
         kw, vw = OQ.unpack_layer(got, layer, amap, opl, H, d)
         assert np.array_equal(Ko[layer].cpu().numpy().view(np.int16), kw.view(np.int16))
         assert np.array_equal(Vo[layer].cpu().numpy().view(np.int16), vw.view(np.int16))
+
+
+def _every_scale_rows(qmax, d, seed):
+    """One row per non-negative finite fp16 absmax (31,744 rows): row r has
+    max |x| = the fp16 with bits r, placed at a random element with a random
+    sign, so every scale the quantizer can produce (fp16 subnormal scales,
+    underflow to 0, the largest) occurs; the other elements are uniform in
+    [-a, a] with a quarter of them at the half-steps (k + 1/2) s, where the
+    rounding of the code is decided by the last bit of the quotient."""
+    rng = np.random.default_rng(seed)
+    a = np.arange(0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    rows = a.size
+    s = (a / np.float32(qmax)).astype(np.float16).astype(np.float32)
+    x = rng.uniform(-1.0, 1.0, (rows, d)).astype(np.float32) * a[:, None]
+    k = rng.integers(-qmax, qmax, size=(rows, d)).astype(np.float32)
+    half = (k + np.float32(0.5)) * s[:, None]
+    tie = rng.random((rows, d)) < 0.25
+    x = np.where(tie, np.clip(half, -a[:, None], a[:, None]), x)
+    x = x.astype(np.float16)
+    at = rng.integers(0, d, size=rows)
+    sign = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=rows)
+    x[np.arange(rows), at] = (sign * a).astype(np.float16)
+    return x
+
+
+@pytest.mark.parametrize("qmax,b,d", [(127, 0.5, 128), (7, 0.25, 128), (127, 0.5, 64), (7, 0.25, 256)])
+def test_every_fp16_scale(qmax, b, d):
+    """Every tier-row absmax an fp16 row can have, all tokens in one
+    quantized tier: payload bytes and dequantized KV bit-exact against the
+    oracle."""
+    H = 2
+    rows = _every_scale_rows(qmax, d, seed=qmax * 1000 + d)
+    n = rows.shape[0] // (2 * H)
+    say("every fp16 scale", dict(qmax=qmax, d=d, n=n))
+    K = np.ascontiguousarray(rows[: n * H].reshape(1, n, H, d))
+    V = np.ascontiguousarray(rows[n * H:].reshape(1, n, H, d))
+    shape = sk.Shape(1, 4, H, d)
+    pl = sk.plan_make(shape, sk.Policy(n, 0, 1, b))
+    opl = OP.make_plan(1, 4, H, d, n, 0, b, 1)
+    assert (opl.n8, opl.n4) == ((n, 0) if qmax == 127 else (0, n))
+    amap, _ = _oracle_map(opl, n, 3)
+    want = OQ.pack(K, V, amap, opl)
+    Kd, Vd = to_dev(K), to_dev(V)
+    md = to_dev(amap.view(np.int32))
+    buf = Guarded(pl.payload_bytes)
+    sk.pack(shape, pl, Kd, Vd, md, None, buf.bytes)
+    torch.cuda.synchronize()
+    buf.check()
+    got = buf.bytes.cpu().numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} payload bytes differ, first at {bad[:5]}"
+    Kw, Vw = OQ.unpack_dense(want, amap, opl, 1, H, d)
+    Ko = torch.empty_like(Kd)
+    Vo = torch.empty_like(Vd)
+    sk.unpack(shape, pl, buf.bytes, md, Ko, Vo)
+    torch.cuda.synchronize()
+    assert np.array_equal(Ko.cpu().numpy().view(np.int16), Kw.view(np.int16))
+    assert np.array_equal(Vo.cpu().numpy().view(np.int16), Vw.view(np.int16))
