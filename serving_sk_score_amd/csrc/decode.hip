@@ -8,10 +8,11 @@
 //
 // The work is bound by reading the payload (about half the fp16 bytes at
 // b = 0.5).  Per element the vector ALUs only dequantize: fp16 bit patterns
-// 1024 + u are built with v_perm_b32 (u = code + 128 for int8, code + 8 for
-// int4), the bias is removed with one packed fp16 add and the scale applied
-// with one packed fp16 multiply (exact integers, one correctly rounded
-// product).  The contractions go elsewhere:
+// 1024 + u (u = code + 128 for int8, code + 8 for int4) are built with
+// v_perm_b32 (int8) or v_and_or_b32 (int4, two channels i and i + 4 at a
+// time), the bias is removed with one packed fp16 add (or fma) and the
+// scale applied with one packed fp16 multiply (exact integers, one
+// correctly rounded product).  The contractions go elsewhere:
 //   - q.k runs on the matrix cores: S^T = K Q^T with v_mfma_f32_32x32x16_f16,
 //     32 tokens per row block and the query group's G = H_q/H_kv heads as
 //     columns (held in VGPRs for the whole wavefront; the other 32 - G
@@ -68,20 +69,50 @@ __device__ __forceinline__ void deq8(uint32_t w, h2 s, uint32_t& lo, uint32_t& h
     hi = as_u32(b * s);
 }
 
-// Eight int4 codes (element 2m in the low nibble of byte m) -> four dwords
-// of fp16 pairs.
-__device__ __forceinline__ void deq4(uint32_t w, h2 s, uint32_t (&o)[4]) {
-    const uint32_t u = w ^ 0x88888888u;           // code + 8 per nibble
-    const uint32_t x = u & 0x0F0F0F0Fu;           // elements 0, 2, 4, 6
-    const uint32_t y = (u >> 4) & 0x0F0F0F0Fu;    // elements 1, 3, 5, 7
-    const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const uint32_t sel[4] = {0x0C040C00u, 0x0C050C01u, 0x0C060C02u, 0x0C070C03u};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const h2 a = as_h2(__builtin_amdgcn_perm(y, x, sel[k]) | 0x64006400u) + bias;
-        o[k] = as_u32(a * s);
-    }
+// (a & m) | c in one instruction.  Written out because the compiler splits
+// it into an and and an or when both constants are literals (a VOP3
+// instruction on this target takes no literal operand), and merges the mask
+// into a preceding xor instead.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
 }
+
+// Eight int4 codes (element 2m in the low nibble of byte m) -> four dwords
+// of fp16 pairs, in the order (e0, e4), (e1, e5), (e2, e6), (e3, e7): the
+// pair of elements i and i + 4 sits at bits 4i and 4i + 16 of the dword, so
+// one v_and_or_b32 with a mask per pair places both nibbles under the 0x64
+// exponent bytes (bits 0-3 for even i after a shift by 8 for i >= 2).  The
+// low nibble of a byte gives 1024 + u, the high one 1024 + 16u, whose
+// packed fma with 1/16 (exact) and -72 returns u - 8 in one step.  The
+// caller keeps track of that channel order (q for K, the output for V).
+__device__ __forceinline__ void deq4(uint32_t w, h2 s, uint32_t (&o)[4]) {
+    const uint32_t u = w ^ 0x88888888u;  // code + 8 per nibble
+    const uint32_t u2 = u >> 8;
+    const h2 lo_bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2 hi_mul = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 hi_bias = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const h2 a0 = as_h2(and_or(u, 0x000F000Fu, 0x64006400u)) + lo_bias;    // e0, e4
+    const h2 a1 = __builtin_elementwise_fma(as_h2(and_or(u, 0x00F000F0u, 0x64006400u)), hi_mul,
+                                            hi_bias);                         // e1, e5
+    const h2 a2 = as_h2(and_or(u2, 0x000F000Fu, 0x64006400u)) + lo_bias;   // e2, e6
+    const h2 a3 = __builtin_elementwise_fma(as_h2(and_or(u2, 0x00F000F0u, 0x64006400u)), hi_mul,
+                                            hi_bias);                         // e3, e7
+    o[0] = as_u32(a0 * s);
+    o[1] = as_u32(a1 * s);
+    o[2] = as_u32(a2 * s);
+    o[3] = as_u32(a3 * s);
+}
+
+// Channel of the first element of fp16 pair w of a dequantized row (the
+// second is this + 1, or + 4 for int4, whose pairs come in deq4's order).
+template <int TIER>
+__device__ __forceinline__ int pair_channel(int w) {
+    return TIER == 2 ? 8 * (w >> 2) + (w & 3) : 2 * w;
+}
+template <int TIER>
+constexpr int pair_step() { return TIER == 2 ? 4 : 1; }
 
 // Row bytes per tier and the number of fp16 pairs one 16-byte piece yields.
 template <int D, int TIER>
@@ -190,6 +221,13 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
         for (int kk = 0; kk < KK; ++kk) {
             u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 4 * kk);
             if (r >= G) v = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (TIER == 2) {
+                // dims 0..7 of the group in deq4's order 0, 4, 1, 5, 2, 6, 3, 7
+                v = u32x4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                          __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                          __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                          __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+            }
             qb[kk] = __builtin_bit_cast(h8, v);
         }
     }
@@ -310,11 +348,14 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
     //    registers; measured, it pays even where it leaves one wave per SIMD,
     //    8 pieces per half row: fp16 at d = 128).
     //  - d = 256 (kSplitV): both blocks' K run through the MFMAs, then each
-    //    block's V goes through one 32-row LDS tile in turn, and both blocks
-    //    are loaded at the tile's start (no prefetch).  Halving the LDS tile
-    //    and the load registers lets two wavefronts share a SIMD: the
+    //    block's V goes through one 32-row LDS tile in turn.  Halving the LDS
+    //    tile and the load registers lets two wavefronts share a SIMD: the
     //    Gemma-shaped call went from 42% to 48.6% of the HBM peak, while at
-    //    d = 128 this order was 1-3% slower than the one above.
+    //    d = 128 this order was 1-3% slower than the one above.  Both blocks
+    //    are loaded at the tile's start: loading the next tile's K and V
+    //    into the same registers as soon as this tile's are consumed keeps
+    //    them live through the softmax and p.V, and needed more registers
+    //    than two wavefronts per SIMD leave (spills at every tier).
     // (The prefetch is a compile-time choice: a load issued on one branch
     // only would make the wait counts of the merged paths conservative.)
     constexpr bool PREF = !kSplitV && NPH <= 8;
@@ -445,9 +486,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
             float* rec = recs + h * hstride;
 #pragma unroll
             for (int k = 0; k < DWL; ++k) {
-                const int w = lane + k * LPT;
-                rec[2 + 2 * w] = o[h][k][0];
-                rec[2 + 2 * w + 1] = o[h][k][1];
+                const int c = pair_channel<TIER>(lane + k * LPT);
+                rec[2 + c] = o[h][k][0];
+                rec[2 + c + pair_step<TIER>()] = o[h][k][1];
             }
         }
     }
