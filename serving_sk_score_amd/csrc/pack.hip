@@ -254,18 +254,41 @@ __global__ __launch_bounds__(kWaves * 64) void pack_kernel(
     }
 }
 
-__device__ __forceinline__ uint32_t deq_pair(int q0, int q1, float s) {
-    const __half a = __float2half_rn((float)q0 * s);  // exact product, one rounding
-    const __half b = __float2half_rn((float)q1 * s);
-    return (uint32_t)__half_as_ushort(a) | ((uint32_t)__half_as_ushort(b) << 16);
+// Dequantization to fp16_rne(code * s) with packed fp16 arithmetic: the
+// code becomes the exact fp16 integer 1024 + u (u = code + bias, the 0x64
+// exponent byte placed above it), the bias is removed exactly, and one
+// packed multiply rounds the exact product code * s once (fp16 subnormals
+// and overflow to inf as IEEE fp16 multiplication gives them).
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Four int8 codes -> two dwords of fp16 pairs (elements 0, 1 and 2, 3).
+__device__ __forceinline__ uint2 deq8x4(uint32_t w, h2 s) {
+    const uint32_t u = w ^ 0x80808080u;  // code + 128 per byte
+    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const h2 a = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + bias;
+    const h2 b = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + bias;
+    return make_uint2(as_u32(a * s), as_u32(b * s));
 }
 
-__device__ __forceinline__ int sext8(uint32_t w, int byte) {
-    return (int)(int8_t)((w >> (8 * byte)) & 0xFFu);
-}
-
-__device__ __forceinline__ int sext4(uint32_t w, int nib) {
-    return ((int)(w << (28 - 4 * nib))) >> 28;
+// Eight int4 codes (element 2m in the low nibble of byte m) -> four dwords
+// of fp16 pairs in element order: byte m is copied under both exponent
+// bytes, the mask keeps its low nibble in the first half (1024 + u) and its
+// high nibble in the second (1024 + 16u), and one packed fma with (1, 1/16)
+// and (-1032, -72) returns both codes exactly.
+__device__ __forceinline__ uint4 deq4x8(uint32_t w, h2 s) {
+    const uint32_t u = w ^ 0x88888888u;  // code + 8 per nibble
+    const h2 mul = {(_Float16)1.0f, (_Float16)0.0625f};
+    const h2 bias = {(_Float16)-1032.0f, (_Float16)-72.0f};
+    uint32_t o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t sel = 0x04000400u | ((uint32_t)m * 0x00010001u);  // [b_m, 0x64, b_m, 0x64]
+        const uint32_t t = __builtin_amdgcn_perm(0x64646464u, u, sel) & 0xFFF0FF0Fu;
+        o[m] = as_u32(__builtin_elementwise_fma(as_h2(t), mul, bias) * s);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 template <int D, int NB, bool PAGED>
@@ -300,7 +323,7 @@ __global__ __launch_bounds__(kWaves * 64) void unpack_kernel(
         // (non-temporal loads: 16% faster on a payload cold in HBM than
         // cached ones); the 2-byte scales share lines and stay cached.
         uint4 c[NB];
-        float sc[NB];
+        uint32_t sc[NB];  // fp16 scale bits
         if (t == 0u) {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
@@ -313,14 +336,14 @@ __global__ __launch_bounds__(kWaves * 64) void unpack_kernel(
                 const int64_t row = rowbase + min(b0 + i * RPP + lane / LPR, rows - 1);
                 const uint2 w = ld_nt8(in + sg.oc[1] + row * D + part * 8);
                 c[i] = make_uint4(w.x, w.y, 0u, 0u);
-                sc[i] = h2f(*reinterpret_cast<const uint16_t*>(in + sg.os[1] + row * 2));
+                sc[i] = *reinterpret_cast<const uint16_t*>(in + sg.os[1] + row * 2);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int64_t row = rowbase + min(b0 + i * RPP + lane / LPR, rows - 1);
                 c[i] = make_uint4(ld_nt4(in + sg.oc[2] + row * (D / 2) + part * 4), 0u, 0u, 0u);
-                sc[i] = h2f(*reinterpret_cast<const uint16_t*>(in + sg.os[2] + row * 2));
+                sc[i] = *reinterpret_cast<const uint16_t*>(in + sg.os[2] + row * 2);
             }
         }
 #pragma unroll
@@ -330,18 +353,12 @@ __global__ __launch_bounds__(kWaves * 64) void unpack_kernel(
             if (t == 0u) {
                 o = c[i];
             } else if (t == 1u) {
-                const float s = sc[i];
-                o.x = deq_pair(sext8(c[i].x, 0), sext8(c[i].x, 1), s);
-                o.y = deq_pair(sext8(c[i].x, 2), sext8(c[i].x, 3), s);
-                o.z = deq_pair(sext8(c[i].y, 0), sext8(c[i].y, 1), s);
-                o.w = deq_pair(sext8(c[i].y, 2), sext8(c[i].y, 3), s);
+                const h2 s = as_h2(sc[i] | (sc[i] << 16));
+                const uint2 lo = deq8x4(c[i].x, s);
+                const uint2 hi = deq8x4(c[i].y, s);
+                o = make_uint4(lo.x, lo.y, hi.x, hi.y);
             } else {
-                const float s = sc[i];
-                const uint32_t w = c[i].x;
-                o.x = deq_pair(sext4(w, 0), sext4(w, 1), s);
-                o.y = deq_pair(sext4(w, 2), sext4(w, 3), s);
-                o.z = deq_pair(sext4(w, 4), sext4(w, 5), s);
-                o.w = deq_pair(sext4(w, 6), sext4(w, 7), s);
+                o = deq4x8(c[i].x, as_h2(sc[i] | (sc[i] << 16)));
             }
             if (r < rows)
                 st_nt(o, (r < H ? Ko : Vo) + (dstrow + (r < H ? r : r - H)) * D + part * 8);
