@@ -12,22 +12,24 @@
 // v_perm_b32 (int8) or v_and_or_b32 (int4, two channels i and i + 4 at a
 // time), the bias is removed with one packed fp16 add (or fma) and the
 // scale applied with one packed fp16 multiply (exact integers, one
-// correctly rounded product).  The contractions go elsewhere:
-//   - q.k runs on the matrix cores: S^T = K Q^T with v_mfma_f32_32x32x16_f16,
-//     32 tokens per row block and the query group's G = H_q/H_kv heads as
-//     columns (held in VGPRs for the whole wavefront; the other 32 - G
-//     columns are zero).  Lane l loads token l%32 of a block and half l/32
-//     of the head dimension, which is exactly the A operand layout when the
-//     contraction runs over the dims of each half in turn.
-//   - p.V runs on the vector ALUs with v_dot2_f32_f16 on (two tokens' values
-//     of one channel, their probabilities rounded to fp16); the dequantized
-//     V rows go through LDS so that lanes can own channel pairs.
+// correctly rounded product).  The contractions go to the matrix cores.
+// Two bodies compute the same values:
+//   - partial_mfma (d = 128, and d = 256 except fp16 rows): both q.k and
+//     p.V on v_mfma_f32_16x16x32_f16, the probabilities kept in the lanes
+//     that computed them, V read back from LDS with the transposing read
+//     (described at that function);
+//   - partial_body (d = 64, and fp16 rows at d = 256): q.k as S^T = K Q^T on
+//     v_mfma_f32_32x32x16_f16, 32 tokens per row block and the query
+//     group's G = H_q/H_kv heads as columns (held in VGPRs; the other
+//     32 - G columns are zero), lane l loading token l%32 and half l/32 of
+//     the head dimension (the A operand layout when the contraction runs
+//     over the dims of each half in turn); p.V on the vector ALUs with
+//     v_dot2_f32_f16 over token pairs, the dequantized V rows staged in LDS
+//     so that lanes own channel pairs.
 // Softmax is online per head across the chunk's 64-token tiles, base 2
-// (c2 = log2(e)/sqrt(d)); a lane of the S^T fragment owns one head, so the
-// running max and sum stay in registers and only the rescale factor is
-// broadcast.  One wavefront per (layer, KV head, tier, chunk of 64*T slots)
-// writes (m, l, o[d]) per query head; merge_kernel combines the chunks of
-// every tier of a (layer, head) in a fixed order.
+// (c2 = log2(e)/sqrt(d)).  One wavefront per (layer, KV head, tier, chunk of
+// 64*T slots) writes (m, l, o[d]) per query head; merge_kernel combines the
+// chunks of every tier of a (layer, head) in a fixed order.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -167,6 +169,7 @@ struct PartialArgs {
 };
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ h8 pairs_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -494,6 +497,284 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const TierArg
     }
 }
 
+// Decode attention with both contractions on the matrix cores, on
+// v_mfma_f32_16x16x32_f16 (per 64-lane wavefront: A holds row l%16 with
+// k = 8*(l/16) .. +7, B holds column l%16 with the same k, and D[4*(l/16)+i]
+// [l%16] sits in lane l).  Lane l works on column c = l%16 and lane group
+// q = l/16:
+//   - S^T = K Q^T per 16-token tile: A = K (row = token c of the tile, its
+//     quarter q of the dims, d/32 MFMAs), B = Q^T (column = head c of the
+//     group, zero past G), so lane l ends with the scores of head c for the
+//     tokens 4q .. 4q+3 of the tile;
+//   - softmax per head: the lane's 16 scores of a 64-token tile, then a max
+//     over the four lanes of its head (l, l^16, l^32, l^48);
+//   - O^T = V^T P^T per 32-token block: B = P^T is exactly the lane's own
+//     probabilities (k = 8q + j: token 4q + j of the block's first tile for
+//     j < 4, token 16 + 4q + j - 4 of its second), A = V^T comes from the
+//     token-major V rows in LDS through ds_read_b64_tr_b16, which hands lane
+//     j of a 16-lane group element j%4 of the 8-byte read of lane 4r+j/4,
+//     r = 0..3: with lane 4r+s reading token T0+r, channels c0+4s .. +3,
+//     lane j gets channel c0+j of tokens T0 .. T0+3, the same k order;
+//     D is O^T: lane l holds channels 16t + 4q + i of head c, so the online
+//     softmax rescale stays in the lane.
+// Against the VALU form above this takes the p.V dot products (about a
+// quarter of the VALU instructions) and half the exponentials (16 instead of
+// 32 per lane and tile: a 16-column tile wastes less on a small query group)
+// off the vector ALUs.  The dequantized values, the fp16 probabilities and
+// the fp32 accumulation are the same.
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+template <int D>
+constexpr int mfma_vt_pitch() { return D + 16; }  // halfs: 2D + 32 bytes, so the
+                                                  // 8 rows of a half-wave's
+                                                  // transposing reads hit 8
+                                                  // disjoint bank groups
+
+// Channel held at position p of a dequantized row (int4 rows come in deq4's
+// pair order: positions 2m, 2m+1 of each group of 8 hold channels m, m + 4).
+template <int TIER>
+__device__ __forceinline__ int pos_channel(int p) {
+    return TIER == 2 ? (p & ~7) + ((p >> 1) & 3) + 4 * (p & 1) : p;
+}
+
+template <int NPQ>
+struct QuarterRegs {
+    u32x4 k[2][NPQ], v[2][NPQ];  // [16-token tile][16-byte piece]
+    uint16_t sk[2], sv[2];
+};
+
+template <int D, int TIER>
+__device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArgs& ta,
+                                             int64_t chunk, _Float16* vt) {
+    using TI = Tier<D, TIER>;
+    constexpr int DQ = D / 4;            // dims of a quarter row
+    constexpr int QBYTES = TI::RB / 4;   // its bytes
+    constexpr int NPQ = QBYTES / 16;     // its 16-byte pieces
+    constexpr int PPP = TI::PPP;         // fp16 pairs per piece
+    constexpr int KC = D / 32;           // MFMAs per S^T tile
+    constexpr int CT = D / 16;           // channel tiles of O^T
+    constexpr int PV = mfma_vt_pitch<D>();
+    static_assert(NPQ >= 1 && NPQ * PPP / 4 == KC, "a quarter row feeds the S^T MFMAs");
+
+    const int lane = threadIdx.x;
+    const int c = lane & 15;   // token of a tile (K, V), head (Q, S, P, O), channel (V^T)
+    const int q = lane >> 4;   // lane group
+    const int g = blockIdx.y;
+    const int li = blockIdx.z;
+    const int64_t layer = a.layer0 + li;
+    const int G = a.G;
+    const int64_t N = ta.N;
+
+    // Q^T as the B operand of S^T: column c = head g*G + c (zero past G), k =
+    // dims DQ*q + 8*kc .. +7
+    h8 qb[KC];
+    {
+        const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q) +
+                               ((int64_t)li * a.Hq + (int64_t)g * G + (c < G ? c : 0)) * (D / 2) +
+                               q * (DQ / 2);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 4 * kc);
+            if (c >= G) v = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (TIER == 2) {
+                v = u32x4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                          __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                          __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                          __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+            }
+            qb[kc] = __builtin_bit_cast(h8, v);
+        }
+    }
+
+    const uint8_t* code = a.payload + ta.off_code + q * QBYTES;
+    const uint16_t* scale = reinterpret_cast<const uint16_t*>(a.payload + ta.off_scale);
+    // the loads of the 32-token block from slot b0: quarter q of the K and V
+    // rows of tokens b0 + c and b0 + 16 + c (slots past the tier's end re-load
+    // its last token; they are masked)
+    auto load_block = [&](QuarterRegs<NPQ>& R, int64_t b0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int64_t slot = b0 + 16 * t + c < N ? b0 + 16 * t + c : N - 1;
+            const int64_t rowK = ((layer * N + slot) * 2) * a.H + g;
+            const int64_t rowV = rowK + a.H;
+#pragma unroll
+            for (int i = 0; i < NPQ; ++i) {
+                R.k[t][i] = ld16(code + rowK * TI::RB + i * 16);
+                R.v[t][i] = ld16(code + rowV * TI::RB + i * 16);
+            }
+            if constexpr (TIER != 0) {
+                R.sk[t] = scale[rowK];
+                R.sv[t] = scale[rowV];
+            }
+        }
+    };
+    auto scale2 = [&](uint16_t bits) -> h2 {
+        if constexpr (TIER == 0) {
+            return h2{(_Float16)1.0f, (_Float16)1.0f};
+        } else {
+            uint32_t sb = bits;
+            asm volatile("" : "+v"(sb));  // consumed here, not where it was loaded
+            return as_h2(sb | (sb << 16));
+        }
+    };
+    // S^T of the block's two 16-token tiles
+    auto s_block = [&](const QuarterRegs<NPQ>& R, f4v (&st)[2]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const h2 sk2 = scale2(R.sk[t]);
+            f4v acc = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < NPQ; ++i) {
+                uint32_t pr[PPP];
+                piece_pairs<D, TIER>(R.k[t][i], sk2, pr);
+#pragma unroll
+                for (int j = 0; j < PPP / 4; ++j)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        pairs_h8(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]),
+                        qb[i * (PPP / 4) + j], acc, 0, 0, 0);
+            }
+            st[t] = acc;
+        }
+    };
+    // the block's dequantized V rows into LDS (row = token of the block)
+    auto v_block = [&](const QuarterRegs<NPQ>& R) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const h2 sv2 = scale2(R.sv[t]);
+            _Float16* vrow = vt + (16 * t + c) * PV + DQ * q;
+#pragma unroll
+            for (int i = 0; i < NPQ; ++i) {
+                uint32_t pv[PPP];
+                piece_pairs<D, TIER>(R.v[t][i], sv2, pv);
+#pragma unroll
+                for (int e = 0; e < PPP; e += 4)
+                    *reinterpret_cast<u32x4*>(vrow + 2 * (i * PPP + e)) =
+                        u32x4{pv[e], pv[e + 1], pv[e + 2], pv[e + 3]};
+            }
+        }
+    };
+
+    float m = -INFINITY, lsum = 0.0f;  // head c, base-2 domain; lsum over this lane's tokens
+    f4v o[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) o[t] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+    // this lane's transposing-read address: token 4q + c/4, channels 4*(c%4) ..
+    _Float16* vrd = vt + (4 * q + (c >> 2)) * PV + 4 * (c & 3);
+
+    QuarterRegs<NPQ> A, B;
+    auto tile_body = [&](auto masked, int64_t s0) {
+        constexpr bool MASKED = decltype(masked)::value;
+        load_block(A, s0);
+        load_block(B, s0 + 32);
+        f4v st[2][2];
+        s_block(A, st[0]);
+        s_block(B, st[1]);
+        // lane: head c, tokens 32*blk + 16*t + 4*q + i of the tile
+        if constexpr (MASKED) {
+            const int rem = (int)(N - s0);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (32 * blk + 16 * t + 4 * q + i >= rem) st[blk][t][i] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[blk][t][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m, mx * a.c2);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile
+        m = mn;
+        // probabilities, rounded to fp16 once: the B operand of each block's
+        // O^T MFMAs and the terms of the denominator
+        h8 pb[2];
+        float ps = 0.0f;
+        const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            uint32_t pw[4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    h2 pr;
+                    pr.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(st[blk][t][i], a.c2, -mn));
+                    pr.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(st[blk][t][i + 1], a.c2, -mn));
+                    ps = __builtin_amdgcn_fdot2(pr, ones, ps, false);
+                    pw[2 * t + i / 2] = as_u32(pr);
+                }
+            pb[blk] = pairs_h8(pw[0], pw[1], pw[2], pw[3]);
+        }
+        lsum = lsum * alpha + ps;
+        if (!__all(alpha == 1.0f)) {
+#pragma unroll
+            for (int t = 0; t < CT; ++t) o[t] *= alpha;
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            v_block(blk == 0 ? A : B);
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < CT; ++t) {
+                typedef __attribute__((address_space(3))) v4s lds_v4s;
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4s*)(vrd + 16 * t));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4s*)(vrd + 16 * PV + 16 * t));
+                const h8 va = __builtin_shufflevector(__builtin_bit_cast(h4, lo),
+                                                      __builtin_bit_cast(h4, hi), 0, 1, 2, 3,
+                                                      4, 5, 6, 7);
+                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[blk], o[t], 0, 0, 0);
+            }
+            __syncthreads();
+        }
+    };
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    const int64_t c0 = chunk * a.T * 64;
+    const int64_t c1 = c0 + a.T * 64 < N ? c0 + a.T * 64 : N;  // end of this chunk
+    const int64_t nfull = (c1 - c0) / 64;                       // whole tiles
+    int64_t s0 = c0;
+    for (int64_t t = 0; t < nfull; ++t, s0 += 64) tile_body(no{}, s0);
+    if (s0 < c1) tile_body(yes{}, s0);
+
+    // the four lanes of a head hold disjoint tokens' sums
+    float ltot = lsum + __shfl_xor(lsum, 16, 64);
+    ltot += __shfl_xor(ltot, 32, 64);
+    float* rec = a.part + (((int64_t)li * a.Hq + (int64_t)g * G + c) * a.NC + ta.chunk_base +
+                           chunk) * (D + 2);
+    if (c < G) {
+        if (q == 0) {
+            rec[0] = m;
+            rec[1] = ltot;
+        }
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rec[2 + pos_channel<TIER>(16 * t + 4 * q + i)] = o[t][i];
+    }
+}
+
+// The matrix-core body covers d = 128 and 256 except fp16 rows at d = 256,
+// whose two blocks of quarter rows would need 256 load registers.
+template <int D, int TIER>
+constexpr bool use_mfma_body() { return D >= 128 && !(D == 256 && TIER == 0); }
+
+template <int D, int TIER>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(PartialArgs a) {
+    __shared__ __align__(16) _Float16 vt[32 * mfma_vt_pitch<D>()];
+    partial_mfma<D, TIER>(a, a.tier[TIER], blockIdx.x, vt);
+}
+
 // One launch per tier (a single kernel holding all three bodies would need
 // registers for their union): blockIdx.x is the chunk within the tier.
 template <int D, int TIER, int GM>
@@ -559,6 +840,10 @@ hipError_t launch_tier(const PartialArgs& a, int nl, int GM, hipStream_t st) {
     const int64_t chunks = a.cend[TIER] - a.tier[TIER].chunk_base;
     if (chunks == 0) return hipSuccess;
     const dim3 grid((unsigned)chunks, (unsigned)a.H, (unsigned)nl);
+    if constexpr (use_mfma_body<D, TIER>()) {
+        decode_mfma_kernel<D, TIER><<<grid, 64, 0, st>>>(a);
+        return hipGetLastError();
+    }
     switch (GM) {
         case 1: decode_partial_kernel<D, TIER, 1><<<grid, 64, 0, st>>>(a); break;
         case 2: decode_partial_kernel<D, TIER, 2><<<grid, 64, 0, st>>>(a); break;
