@@ -544,9 +544,9 @@ struct QuarterRegs {
     uint16_t sk[2], sv[2];
 };
 
-template <int D, int TIER>
+template <int D, int TIER, bool P4>
 __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArgs& ta,
-                                             int64_t chunk, _Float16* vt) {
+                                             int64_t chunk, _Float16* vt, _Float16* pt) {
     using TI = Tier<D, TIER>;
     constexpr int DQ = D / 4;            // dims of a quarter row
     constexpr int QBYTES = TI::RB / 4;   // its bytes
@@ -656,11 +656,17 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
     };
 
     float m = -INFINITY, lsum = 0.0f;  // head c, base-2 domain; lsum over this lane's tokens
-    f4v o[CT];
+    // O^T accumulators: CT 16x16 tiles, or with P4 (G <= 4) D/64 groups of
+    // the 4x4x4 form, whose lane l holds channels 64*mg + 4*(l/4) + i of head
+    // l%4
+    constexpr int NO = P4 ? D / 64 : CT;
+    f4v o[NO];
 #pragma unroll
-    for (int t = 0; t < CT; ++t) o[t] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NO; ++t) o[t] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
     // this lane's transposing-read address: token 4q + c/4, channels 4*(c%4) ..
-    _Float16* vrd = vt + (4 * q + (c >> 2)) * PV + 4 * (c & 3);
+    // (with P4: token c/4, channels 16q + 4*(c%4) .., 64 channels per group)
+    _Float16* vrd = P4 ? vt + (c >> 2) * PV + 16 * q + 4 * (c & 3)
+                       : vt + (4 * q + (c >> 2)) * PV + 4 * (c & 3);
 
     QuarterRegs<NPQ> A, B;
     auto tile_body = [&](auto masked, int64_t s0) {
@@ -714,7 +720,24 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
             pb[blk] = pairs_h8(pw[0], pw[1], pw[2], pw[3]);
         }
         lsum = lsum * alpha + ps;
-        if (!__all(alpha == 1.0f)) {
+        if constexpr (P4) {
+            // this tile's probabilities of heads 0..3 by token, for the B
+            // operand of the 4x4x4 form (lane l reads head l%4)
+            if (c < 4) {
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        *reinterpret_cast<uint2*>(pt + c * 64 + 32 * blk + 16 * t + 4 * q) =
+                            make_uint2(__builtin_bit_cast(u32x4, pb[blk])[2 * t],
+                                       __builtin_bit_cast(u32x4, pb[blk])[2 * t + 1]);
+            }
+            const float al = __shfl(alpha, lane & 3, 64);
+            if (!__all(al == 1.0f)) {
+#pragma unroll
+                for (int t = 0; t < NO; ++t) o[t] *= al;
+            }
+        } else if (!__all(alpha == 1.0f)) {
 #pragma unroll
             for (int t = 0; t < CT; ++t) o[t] *= alpha;
         }
@@ -722,17 +745,37 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
         for (int blk = 0; blk < 2; ++blk) {
             v_block(blk == 0 ? A : B);
             __syncthreads();
+            typedef __attribute__((address_space(3))) v4s lds_v4s;
+            if constexpr (P4) {
+                // 4x4x4 form, 16 blocks per instruction: block b = l/4 holds
+                // channels 64*mg + 4b .. +3 (rows, A from the transposing
+                // read: lane 4b + i gets channel 64*mg + 4b + i of 4 tokens)
+                // by heads 0..3 (columns, B: lane 4b + j gets head j's 4
+                // probabilities), k = 4 tokens per step
 #pragma unroll
-            for (int t = 0; t < CT; ++t) {
-                typedef __attribute__((address_space(3))) v4s lds_v4s;
-                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4s*)(vrd + 16 * t));
-                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4s*)(vrd + 16 * PV + 16 * t));
-                const h8 va = __builtin_shufflevector(__builtin_bit_cast(h4, lo),
-                                                      __builtin_bit_cast(h4, hi), 0, 1, 2, 3,
-                                                      4, 5, 6, 7);
-                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[blk], o[t], 0, 0, 0);
+                for (int kk = 0; kk < 8; ++kk) {
+                    const h4 pj = *reinterpret_cast<const h4*>(pt + (lane & 3) * 64 + 32 * blk +
+                                                               4 * kk);
+#pragma unroll
+                    for (int mg = 0; mg < NO; ++mg) {
+                        const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_v4s*)(vrd + 4 * kk * PV + 64 * mg));
+                        o[mg] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                            __builtin_bit_cast(h4, va), pj, o[mg], 0, 0, 0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < CT; ++t) {
+                    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_v4s*)(vrd + 16 * t));
+                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_v4s*)(vrd + 16 * PV + 16 * t));
+                    const h8 va = __builtin_shufflevector(__builtin_bit_cast(h4, lo),
+                                                          __builtin_bit_cast(h4, hi), 0, 1, 2,
+                                                          3, 4, 5, 6, 7);
+                    o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[blk], o[t], 0, 0, 0);
+                }
             }
             __syncthreads();
         }
@@ -750,17 +793,29 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
     // the four lanes of a head hold disjoint tokens' sums
     float ltot = lsum + __shfl_xor(lsum, 16, 64);
     ltot += __shfl_xor(ltot, 32, 64);
-    float* rec = a.part + (((int64_t)li * a.Hq + (int64_t)g * G + c) * a.NC + ta.chunk_base +
-                           chunk) * (D + 2);
-    if (c < G) {
-        if (q == 0) {
-            rec[0] = m;
-            rec[1] = ltot;
+    const int64_t rec0 = (int64_t)li * a.Hq + (int64_t)g * G;  // record row of head 0
+    const int64_t rstride = a.NC * (D + 2);                      // between heads
+    float* rec = a.part + (rec0 * a.NC + ta.chunk_base + chunk) * (D + 2);
+    if (c < G && q == 0) {
+        rec[c * rstride] = m;
+        rec[c * rstride + 1] = ltot;
+    }
+    if constexpr (P4) {
+        const int j = lane & 3;  // head
+        if (j < G) {
+#pragma unroll
+            for (int mg = 0; mg < NO; ++mg)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    rec[j * rstride + 2 + pos_channel<TIER>(64 * mg + 4 * (lane >> 2) + i)] =
+                        o[mg][i];
         }
+    } else if (c < G) {
 #pragma unroll
         for (int t = 0; t < CT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rec[2 + pos_channel<TIER>(16 * t + 4 * q + i)] = o[t][i];
+            for (int i = 0; i < 4; ++i)
+                rec[c * rstride + 2 + pos_channel<TIER>(16 * t + 4 * q + i)] = o[t][i];
     }
 }
 
@@ -769,10 +824,11 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
 template <int D, int TIER>
 constexpr bool use_mfma_body() { return D >= 128 && !(D == 256 && TIER == 0); }
 
-template <int D, int TIER>
+template <int D, int TIER, bool P4>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(PartialArgs a) {
     __shared__ __align__(16) _Float16 vt[32 * mfma_vt_pitch<D>()];
-    partial_mfma<D, TIER>(a, a.tier[TIER], blockIdx.x, vt);
+    __shared__ __align__(16) _Float16 pt[P4 ? 4 * 64 : 4];
+    partial_mfma<D, TIER, P4>(a, a.tier[TIER], blockIdx.x, vt, pt);
 }
 
 // One launch per tier (a single kernel holding all three bodies would need
@@ -841,7 +897,10 @@ hipError_t launch_tier(const PartialArgs& a, int nl, int GM, hipStream_t st) {
     if (chunks == 0) return hipSuccess;
     const dim3 grid((unsigned)chunks, (unsigned)a.H, (unsigned)nl);
     if constexpr (use_mfma_body<D, TIER>()) {
-        decode_mfma_kernel<D, TIER><<<grid, 64, 0, st>>>(a);
+        if (GM <= 4)
+            decode_mfma_kernel<D, TIER, true><<<grid, 64, 0, st>>>(a);
+        else
+            decode_mfma_kernel<D, TIER, false><<<grid, 64, 0, st>>>(a);
         return hipGetLastError();
     }
     switch (GM) {
