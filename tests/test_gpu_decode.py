@@ -56,6 +56,11 @@ CASES = [
     (2, 16, 1, 64, 300, 0, 0.25, 1, 0),      # G = 16, all int4
     (2, 8, 4, 128, 1000, 4, 0.3, 0, 1),      # dropped tokens
     (1, 2, 2, 64, 1, 0, 1.0, 1, 0),          # one token
+    # the matrix-core body: 4x4x4 p.V for G <= 4, 16x16x32 above
+    (2, 16, 2, 256, 700, 4, 0.3, 1, 0),      # d = 256, G = 8: int8 + int4
+    (1, 16, 1, 128, 600, 4, 0.45, 1, 0),     # d = 128, G = 16 (the largest group)
+    (2, 4, 4, 128, 333, 4, 0.5, 1, 0),       # d = 128, G = 1
+    (1, 6, 2, 256, 200, 4, 0.4, 1, 0),       # d = 256, G = 3 (4x4x4 with a spare column)
 ]
 
 
