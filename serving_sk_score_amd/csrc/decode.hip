@@ -35,6 +35,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "sk_kernels.h"
@@ -544,9 +545,28 @@ struct QuarterRegs {
     uint16_t sk[2], sv[2];
 };
 
-template <int D, int TIER, bool P4>
+// LDS of one wavefront of the matrix-core body: its V rows, then (P4) the
+// probability table.
+template <int D>
+constexpr size_t mfma_wave_lds() { return (size_t)32 * mfma_vt_pitch<D>() * 2 + 4 * 64 * 2; }
+
+// Ordering of one wavefront's own LDS writes and reads.  The wavefront
+// issues its LDS instructions in order, so only the compiler's code motion
+// has to be stopped; with several wavefronts per workgroup, each on LDS of
+// its own, a workgroup barrier would only make them wait for each other.
+template <bool WG>
+__device__ __forceinline__ void lds_sync() {
+    if constexpr (WG) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    } else {
+        __syncthreads();
+    }
+}
+
+template <int D, int TIER, bool P4, bool WG>
 __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArgs& ta,
-                                             int64_t chunk, _Float16* vt, _Float16* pt) {
+                                             int64_t chunk, int g, _Float16* vt, _Float16* pt) {
     using TI = Tier<D, TIER>;
     constexpr int DQ = D / 4;            // dims of a quarter row
     constexpr int QBYTES = TI::RB / 4;   // its bytes
@@ -557,10 +577,9 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
     constexpr int PV = mfma_vt_pitch<D>();
     static_assert(NPQ >= 1 && NPQ * PPP / 4 == KC, "a quarter row feeds the S^T MFMAs");
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int c = lane & 15;   // token of a tile (K, V), head (Q, S, P, O), channel (V^T)
     const int q = lane >> 4;   // lane group
-    const int g = blockIdx.y;
     const int li = blockIdx.z;
     const int64_t layer = a.layer0 + li;
     const int G = a.G;
@@ -744,7 +763,7 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             v_block(blk == 0 ? A : B);
-            __syncthreads();
+            lds_sync<WG>();
             typedef __attribute__((address_space(3))) v4s lds_v4s;
             if constexpr (P4) {
                 // 4x4x4 form, 16 blocks per instruction: block b = l/4 holds
@@ -777,7 +796,7 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
                     o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[blk], o[t], 0, 0, 0);
                 }
             }
-            __syncthreads();
+            lds_sync<WG>();
         }
     };
 
@@ -828,7 +847,26 @@ template <int D, int TIER, bool P4>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(PartialArgs a) {
     __shared__ __align__(16) _Float16 vt[32 * mfma_vt_pitch<D>()];
     __shared__ __align__(16) _Float16 pt[P4 ? 4 * 64 : 4];
-    partial_mfma<D, TIER, P4>(a, a.tier[TIER], blockIdx.x, vt, pt);
+    partial_mfma<D, TIER, P4, false>(a, a.tier[TIER], blockIdx.x, blockIdx.y, vt, pt);
+}
+
+// KV heads (wavefronts) of a workgroup of the one-per-head form: eight keep
+// the register budget of two wavefronts per SIMD.
+constexpr int kWgMaxHeads = 8;
+// Workgroups a launch needs before the one-per-head form is used: two per CU.
+constexpr int64_t kWgMinGroups = 512;
+
+// One workgroup per (layer, tier, chunk) with one wavefront per KV head:
+// the token rows of a chunk hold every head's K (then V) row side by side,
+// so the wavefronts of a workgroup read them as one contiguous stream
+// instead of one row in 2H per wavefront.
+template <int D, int TIER, bool P4>
+__global__ __launch_bounds__(64 * kWgMaxHeads) void decode_mfma_wg_kernel(PartialArgs a) {
+    extern __shared__ __align__(16) _Float16 lds[];
+    const int w = threadIdx.x >> 6;
+    _Float16* vt = lds + w * (mfma_wave_lds<D>() / 2);
+    _Float16* pt = vt + 32 * mfma_vt_pitch<D>();
+    partial_mfma<D, TIER, P4, true>(a, a.tier[TIER], blockIdx.x, w, vt, pt);
 }
 
 // One launch per tier (a single kernel holding all three bodies would need
@@ -891,12 +929,45 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ par
         lse[(int64_t)li * Hq + h] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
+// LDS a workgroup may take on the current device (read once per device).
+size_t wg_lds_limit() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess ||
+            v <= 0)
+            return 0;
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return (size_t)v;
+}
+
 template <int D, int TIER>
 hipError_t launch_tier(const PartialArgs& a, int nl, int GM, hipStream_t st) {
     const int64_t chunks = a.cend[TIER] - a.tier[TIER].chunk_base;
     if (chunks == 0) return hipSuccess;
     const dim3 grid((unsigned)chunks, (unsigned)a.H, (unsigned)nl);
     if constexpr (use_mfma_body<D, TIER>()) {
+        // The one-per-head workgroups pay at d = 128 when they are enough
+        // to fill the machine twice over (measured: Mistral-shaped int8 tier,
+        // 512 workgroups, 128 -> 110 us).  With fewer, or at d = 256, where
+        // a workgroup takes most of a CU's LDS, they were 3-36% slower than
+        // one wavefront per workgroup.
+        const size_t wg_lds = (size_t)a.H * mfma_wave_lds<D>();
+        if (D == 128 && a.H <= kWgMaxHeads && chunks * nl >= kWgMinGroups &&
+            wg_lds <= wg_lds_limit()) {
+            if constexpr (D == 128) {
+                const dim3 wgrid((unsigned)chunks, 1u, (unsigned)nl);
+                if (GM <= 4)
+                    decode_mfma_wg_kernel<D, TIER, true><<<wgrid, 64 * a.H, wg_lds, st>>>(a);
+                else
+                    decode_mfma_wg_kernel<D, TIER, false><<<wgrid, 64 * a.H, wg_lds, st>>>(a);
+                return hipGetLastError();
+            }
+        }
         if (GM <= 4)
             decode_mfma_kernel<D, TIER, true><<<grid, 64, 0, st>>>(a);
         else

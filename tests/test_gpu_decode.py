@@ -61,6 +61,9 @@ CASES = [
     (1, 16, 1, 128, 600, 4, 0.45, 1, 0),     # d = 128, G = 16 (the largest group)
     (2, 4, 4, 128, 333, 4, 0.5, 1, 0),       # d = 128, G = 1
     (1, 6, 2, 256, 200, 4, 0.4, 1, 0),       # d = 256, G = 3 (4x4x4 with a spare column)
+    # enough chunks x layers (>= 512) for the one-wavefront-per-KV-head workgroups at d = 128
+    (16, 32, 8, 128, 2048, 4, 0.5, 1, 0),    # G = 4, int8 tier: 32 chunks x 16 layers
+    (16, 28, 4, 128, 2600, 4, 0.6, 0, 0),    # G = 7, 2-tier: int8 tier 33 chunks x 16 layers
 ]
 
 
