@@ -547,6 +547,9 @@ struct QuarterRegs {
 
 // LDS of one wavefront of the matrix-core body: its V rows, then (P4) the
 // probability table.
+template <int D, int TIER, bool P4>
+constexpr bool half_v() { return P4 && D == 256 && TIER == 2; }
+
 template <int D>
 constexpr size_t mfma_wave_lds() { return (size_t)32 * mfma_vt_pitch<D>() * 2 + 4 * 64 * 2; }
 
@@ -657,11 +660,12 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
         }
     };
     // the block's dequantized V rows into LDS (row = token of the block)
-    auto v_block = [&](const QuarterRegs<NPQ>& R) {
+    // (tiles t0 .. t1 - 1 of the block, tile t at rows 16 * (t - t0) ..)
+    auto v_block = [&](const QuarterRegs<NPQ>& R, int t0, int t1) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = t0; t < t1; ++t) {
             const h2 sv2 = scale2(R.sv[t]);
-            _Float16* vrow = vt + (16 * t + c) * PV + DQ * q;
+            _Float16* vrow = vt + (16 * (t - t0) + c) * PV + DQ * q;
 #pragma unroll
             for (int i = 0; i < NPQ; ++i) {
                 uint32_t pv[PPP];
@@ -679,6 +683,11 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
     // the 4x4x4 form, whose lane l holds channels 64*mg + 4*(l/4) + i of head
     // l%4
     constexpr int NO = P4 ? D / 64 : CT;
+    // int4 rows at d = 256 stage V 16 tokens at a time in the 4x4x4 form:
+    // 8.7 KB of LDS per wavefront instead of 17, so the three wavefronts per
+    // SIMD that its registers allow fit (538 against 561-570 us on the
+    // Gemma-shaped int4 tier; int8, at two wavefronts either way, lost 15%).
+    constexpr bool HALF_V = half_v<D, TIER, P4>();
     f4v o[NO];
 #pragma unroll
     for (int t = 0; t < NO; ++t) o[t] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -760,30 +769,37 @@ __device__ __forceinline__ void partial_mfma(const PartialArgs& a, const TierArg
 #pragma unroll
             for (int t = 0; t < CT; ++t) o[t] *= alpha;
         }
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            v_block(blk == 0 ? A : B);
-            lds_sync<WG>();
-            typedef __attribute__((address_space(3))) v4s lds_v4s;
             if constexpr (P4) {
                 // 4x4x4 form, 16 blocks per instruction: block b = l/4 holds
                 // channels 64*mg + 4b .. +3 (rows, A from the transposing
                 // read: lane 4b + i gets channel 64*mg + 4b + i of 4 tokens)
                 // by heads 0..3 (columns, B: lane 4b + j gets head j's 4
-                // probabilities), k = 4 tokens per step
+                // probabilities), k = 4 tokens per step; with HALF_V the
+                // block's V goes through LDS one 16-token tile at a time
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const h4 pj = *reinterpret_cast<const h4*>(pt + (lane & 3) * 64 + 32 * blk +
-                                                               4 * kk);
+                for (int h = 0; h < (HALF_V ? 2 : 1); ++h) {
+                    v_block(blk == 0 ? A : B, HALF_V ? h : 0, HALF_V ? h + 1 : 2);
+                    lds_sync<WG>();
 #pragma unroll
-                    for (int mg = 0; mg < NO; ++mg) {
-                        const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_v4s*)(vrd + 4 * kk * PV + 64 * mg));
-                        o[mg] = __builtin_amdgcn_mfma_f32_4x4x4f16(
-                            __builtin_bit_cast(h4, va), pj, o[mg], 0, 0, 0);
+                    for (int kk = 0; kk < (HALF_V ? 4 : 8); ++kk) {
+                        const h4 pj = *reinterpret_cast<const h4*>(
+                            pt + (lane & 3) * 64 + 32 * blk + 16 * h + 4 * kk);
+#pragma unroll
+                        for (int mg = 0; mg < NO; ++mg) {
+                            const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_v4s*)(vrd + 4 * kk * PV + 64 * mg));
+                            o[mg] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                                __builtin_bit_cast(h4, va), pj, o[mg], 0, 0, 0);
+                        }
                     }
+                    if (HALF_V && h == 0) lds_sync<WG>();
                 }
             } else {
+                v_block(blk == 0 ? A : B, 0, 2);
+                lds_sync<WG>();
 #pragma unroll
                 for (int t = 0; t < CT; ++t) {
                     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -845,7 +861,7 @@ constexpr bool use_mfma_body() { return D >= 128 && !(D == 256 && TIER == 0); }
 
 template <int D, int TIER, bool P4>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(PartialArgs a) {
-    __shared__ __align__(16) _Float16 vt[32 * mfma_vt_pitch<D>()];
+    __shared__ __align__(16) _Float16 vt[(half_v<D, TIER, P4>() ? 16 : 32) * mfma_vt_pitch<D>()];
     __shared__ __align__(16) _Float16 pt[P4 ? 4 * 64 : 4];
     partial_mfma<D, TIER, P4, false>(a, a.tier[TIER], blockIdx.x, blockIdx.y, vt, pt);
 }
