@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough budget of the oracle's timed sample")
+    ap.add_argument("--score-launch", choices=("layers", "per-layer"), default="layers",
+                    help="score passes as one launch over all layers of a request, or one "
+                         "launch per layer (the same results, bit for bit)")
     return ap.parse_args()
 
 
@@ -171,6 +174,34 @@ def torch_copy_gbs(torch, nbytes, dev):
     return 2 * nbytes * 3 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
 
+def score_passes(m, sk, per_layer, shape, Q, K, lse, score, cws, pass_flops):
+    """Both score passes of one request, every layer: one launch per pass
+    (sk_score_rowlse_layers / sk_score_colsum_layers) or, with per_layer, a
+    launch per layer and pass.  lse is [L][Hq][n] (rows of layer 0 are used
+    by the per-layer form); each mark carries the flops of what it launched."""
+    L = shape.n_layers
+    if not per_layer:
+        m("rowlse", L * pass_flops, lambda: sk.score_rowlse_layers(shape, Q, K, lse))
+        m("colsum", L * pass_flops,
+          lambda: sk.score_colsum_layers(shape, Q, K, lse, score, False, cws))
+        return
+    shape1 = sk.Shape(1, shape.n_q_heads, shape.n_kv_heads, shape.head_dim)
+    for layer in range(L):
+        m("rowlse", pass_flops, lambda: sk.score_rowlse(shape1, Q[layer], K[layer], lse[0]))
+        m("colsum", pass_flops, lambda: sk.score_colsum(shape1, Q[layer], K[layer], lse[0],
+                                                        score, layer > 0, cws))
+
+
+def score_buffers(torch, sk, shape, n, per_layer, dev):
+    """lse [L][Hq][n] and the colsum workspace for a request of n tokens."""
+    shape1 = sk.Shape(1, shape.n_q_heads, shape.n_kv_heads, shape.head_dim)
+    L = 1 if per_layer else shape.n_layers
+    ws = (sk.colsum_workspace_bytes(shape1, n) if per_layer
+          else sk.colsum_layers_workspace_bytes(shape, n))
+    return (torch.empty(L * shape.n_q_heads * n, dtype=torch.float32, device=dev),
+            torch.empty(max(1, ws), dtype=torch.uint8, device=dev))
+
+
 # --------------------------------------------------------------- batched mix --
 
 def run_batched(cfg, args, dev, torch, sk):
@@ -181,8 +212,8 @@ def run_batched(cfg, args, dev, torch, sk):
     tables, num_blocks = gen.block_tables(cfg, lengths)
     R = len(lengths)
     nmax = max(lengths)
-    shape1 = sk.Shape(1, Hq, Hkv, d)
     shape = sk.Shape(L, Hq, Hkv, d)
+    per_layer = args.score_launch == "per-layer"
     pols = {b: [sk.Policy(n, cfg.sinks, cfg.three_tier, b) for n in lengths] for b in cfg.budgets}
     plans = {b: [sk.plan_make(shape, p) for p in pols[b]] for b in cfg.budgets}
     kv = [2 * L * n * Hkv * d * 2 for n in lengths]
@@ -208,10 +239,8 @@ def run_batched(cfg, args, dev, torch, sk):
     torch.cuda.synchronize()
     log(f"inputs resident in {time.time() - t0:.1f} s")
 
-    lse_all = torch.empty(Hq * nmax, dtype=torch.float32, device=dev)
-    cws = torch.empty(max(1, sk.colsum_workspace_bytes(shape1, nmax)), dtype=torch.uint8,
-                      device=dev)
-    lse = [lse_all[:Hq * n].view(Hq, n) for n in lengths]
+    lse_all, cws = score_buffers(torch, sk, shape, nmax, per_layer, dev)
+    lse = [lse_all[:lse_all.numel() // nmax * n].view(-1, Hq, n) for n in lengths]
     score = [torch.empty(n, dtype=torch.float32, device=dev) for n in lengths]
     amap = [torch.empty(n, dtype=torch.int32, device=dev) for n in lengths]
     order = [torch.empty(n, dtype=torch.int32, device=dev) for n in lengths]
@@ -234,12 +263,8 @@ def run_batched(cfg, args, dev, torch, sk):
 
     def step(m):
         for r in range(R):
-            for layer in range(L):
-                m("rowlse", pass_flops[r],
-                  lambda: sk.score_rowlse(shape1, Q[r][layer], K[r][layer], lse[r]))
-                m("colsum", pass_flops[r],
-                  lambda: sk.score_colsum(shape1, Q[r][layer], K[r][layer], lse[r], score[r],
-                                          layer > 0, cws))
+            score_passes(m, sk, per_layer, shape, Q[r], K[r], lse[r], score[r], cws,
+                         pass_flops[r])
         for b in cfg.budgets:
             for r in range(R):
                 m(f"assign@{b}", 0,
@@ -295,7 +320,7 @@ def run_batched(cfg, args, dev, torch, sk):
     names = score_kernel_names(Hq, Hkv, d)
     dom = "colsum" if cms.sum() >= rms.sum() else "rowlse"
     roof = mfma_rl(*((cfl, cms) if dom == "colsum" else (rfl, rms)), names[dom], cfg.name)
-    roof["launches_per_step"] = R * L
+    roof["launches_per_step"] = R * (L if per_layer else 1)
     nbk = pack_batch(Hkv, d)
 
     per_budget = {}
@@ -315,13 +340,13 @@ def run_batched(cfg, args, dev, torch, sk):
             "unpack_paged": hbm_rl(ub, tu, f"unpack_kernel<{d},{nbk},true>", f"{cfg.name}@{b}", R),
             "assign_ms_per_step": round(am.sum() / K_, 4)}
 
-    # score efficiency per request (launches of all layers and steps)
+    # score efficiency per request (its launches over all steps)
     per_req = []
-    nrl = len(rms) // K_ // R            # = L
+    nrl = len(rms) // K_ // R            # launches per pass and request: 1, or L
     for r, n in enumerate(lengths):
         idx = np.concatenate([np.arange(s * R * nrl + r * nrl, s * R * nrl + (r + 1) * nrl)
                               for s in range(K_)])
-        f = pass_flops[r] * len(idx)
+        f = L * pass_flops[r] * K_
         per_req.append({"n": n, "rowlse_ms": round(float(rms[idx].mean()), 4),
                         "colsum_ms": round(float(cms[idx].mean()), 4),
                         "rowlse_frac": round(f / (rms[idx].sum() * 1e-3) / 1e12
@@ -354,9 +379,12 @@ def run_batched(cfg, args, dev, torch, sk):
         "score_pct_mfma": round(score_tflops / MFMA_F16_PEAK_TFLOPS, 4),
         "score_flops_per_step": float(score_flops),
         "roofline": roof,
-        "roofline_other_pass": mfma_rl(*((rfl, rms) if dom == "colsum" else (cfl, cms)),
-                                       names["rowlse" if dom == "colsum" else "colsum"],
-                                       cfg.name),
+        "roofline_other_pass": dict(mfma_rl(*((rfl, rms) if dom == "colsum" else (cfl, cms)),
+                                            names["rowlse" if dom == "colsum" else "colsum"],
+                                            cfg.name),
+                                    launches_per_step=roof["launches_per_step"]),
+        "score_launch": "one launch per pass and layer" if per_layer else
+                        "one launch per pass over all layers of a request",
         "stage_ms_per_step": {"rowlse": round(rms.sum() / K_, 3),
                               "colsum": round(cms.sum() / K_, 3),
                               "pack": round(t_pack * 1e3, 3),
@@ -372,7 +400,7 @@ def run_batched(cfg, args, dev, torch, sk):
 
 # ----------------------------------------------------------- single request --
 
-def run_single(cfg, steps, warmup, dev, torch, sk, extras):
+def run_single(cfg, steps, warmup, dev, torch, sk, extras, per_layer=False):
     from workloads import gen_device as gd
 
     L, Hq, Hkv, d, n = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.tokens
@@ -389,11 +417,10 @@ def run_single(cfg, steps, warmup, dev, torch, sk, extras):
     log(f"inputs resident in {time.time() - t0:.1f} s")
 
     shape = sk.Shape(L, Hq, Hkv, d)
-    shape1 = sk.Shape(1, Hq, Hkv, d)
     pol = sk.Policy(n, cfg.sinks, cfg.three_tier, cfg.budget)
     plan = sk.plan_make(shape, pol)
-    lse = torch.empty((Hq, n), dtype=torch.float32, device=dev)
-    cws = torch.empty(max(1, sk.colsum_workspace_bytes(shape1, n)), dtype=torch.uint8, device=dev)
+    lse, cws = score_buffers(torch, sk, shape, n, per_layer, dev)
+    lse = lse.view(-1, Hq, n)
     score = torch.empty(n, dtype=torch.float32, device=dev)
     amap = torch.empty(n, dtype=torch.int32, device=dev)
     order = torch.empty(n, dtype=torch.int32, device=dev)
@@ -414,10 +441,7 @@ def run_single(cfg, steps, warmup, dev, torch, sk, extras):
     paged_bytes = unpack_bytes + 4 * nblk
 
     def step(m):
-        for layer in range(L):
-            m("rowlse", pass_flops, lambda: sk.score_rowlse(shape1, Q[layer], K[layer], lse))
-            m("colsum", pass_flops, lambda: sk.score_colsum(shape1, Q[layer], K[layer], lse,
-                                                            score, layer > 0, cws))
+        score_passes(m, sk, per_layer, shape, Q, K, lse, score, cws, pass_flops)
         m("assign", 0, lambda: sk.assign_tiers(pol, plan, score, amap, order))
         scratch.fill_(0x5A)
         m("pack", pack_bytes, lambda: sk.pack(shape, plan, K, V, amap, order, payload))
@@ -465,10 +489,10 @@ def run_single(cfg, steps, warmup, dev, torch, sk, extras):
         "score_tflops": round(score_tflops, 1),
         "score_pct_mfma": round(score_tflops / MFMA_F16_PEAK_TFLOPS, 4),
         "roofline": dict(mfma_rl(*((cfl, cms) if dom == "colsum" else (rfl, rms)), names[dom],
-                                 cfg.name), launches_per_step=L),
+                                 cfg.name), launches_per_step=L if per_layer else 1),
         "roofline_other_pass": dict(mfma_rl(*((rfl, rms) if dom == "colsum" else (cfl, cms)),
                                             names["rowlse" if dom == "colsum" else "colsum"],
-                                            cfg.name), launches_per_step=L),
+                                            cfg.name), launches_per_step=L if per_layer else 1),
         "roofline_stages": {
             "pack": hbm_rl(pack_bytes, per["pack"], f"pack_kernel<{d},{nbk}>", cfg.name),
             "unpack": hbm_rl(unpack_bytes, per["unpack"], f"unpack_kernel<{d},{nbk},false>",
@@ -619,7 +643,8 @@ def main():
     if cfg.requests:
         line, lengths = run_batched(cfg, args, dev, torch, sk)
     else:
-        one = run_single(cfg, args.steps, args.warmup, dev, torch, sk, extras=True)
+        one = run_single(cfg, args.steps, args.warmup, dev, torch, sk, extras=True,
+                         per_layer=args.score_launch == "per-layer")
         lengths = None
         line = {"metric": METRIC, "value": one.pop("value"), "unit": "GB/s", "n_gpus": 1,
                 "steps": args.steps, "warmup": args.warmup, "ms_per_step": one.pop("ms_per_step"),
@@ -632,7 +657,8 @@ def main():
         line["workloads"] = {}
         for w in others:
             line["workloads"][w] = run_single(get_config(w), args.other_steps, 1, dev, torch, sk,
-                                              extras=(w == "mistral7b"))
+                                              extras=(w == "mistral7b"),
+                                              per_layer=args.score_launch == "per-layer")
             gc.collect()
             torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

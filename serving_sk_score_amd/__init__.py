@@ -12,6 +12,7 @@ from .sk import (  # noqa: F401
     SkError, assign_tiers, balanced_keys, colsum_workspace_bytes, decode_attention,
     decode_workspace_bytes, lib, pack,
     plan_make, recency_weight, score, score_colsum, score_kvnorm, score_noalloc, score_rowlse,
-    score_workspace_bytes, unpack, unpack_paged, upgrade_bytes, upgrade_pack, upgrade_unpack,
+    colsum_layers_workspace_bytes, score_colsum_layers, score_layers,
+    score_layers_workspace_bytes, score_rowlse_layers, score_workspace_bytes, unpack, unpack_paged, upgrade_bytes, upgrade_pack, upgrade_unpack,
     upgrade_unpack_paged,
 )

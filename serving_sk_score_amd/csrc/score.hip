@@ -251,6 +251,11 @@ __global__ __launch_bounds__(W * QW * 64, D == 256 ? 1 : 2) void rowlse_kernel(
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int khalf = 8 * (lane >> 5);
+    // layer blockIdx.z of an all-layer launch: Q [L][n][Hq][D], K [L][n][Hkv][D],
+    // lse2 [L][Hq][n]
+    Q += (int64_t)blockIdx.z * n * Hq * D;
+    K += (int64_t)blockIdx.z * n * Hkv * D;
+    lse2 += (int64_t)blockIdx.z * Hq * n;
     const int R = Hq / Hkv;
     const int chunks = R / W;
     const int g = blockIdx.x / chunks;
@@ -444,6 +449,11 @@ __global__ __launch_bounds__(KW * 64, 2) void colsum_kernel(
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int khalf = 8 * (lane >> 5);
+    // layer blockIdx.z of an all-layer launch (partial [L][Hq][ldp])
+    Q += (int64_t)blockIdx.z * n * Hq * D;
+    K += (int64_t)blockIdx.z * n * Hkv * D;
+    lse2 += (int64_t)blockIdx.z * Hq * n;
+    partial += (int64_t)blockIdx.z * Hq * ldp;
     const int h = blockIdx.x;
     const int g = h / (Hq / Hkv);
     const int64_t K0 = (int64_t)blockIdx.y * (kColKeys * KW);  // blockIdx.y = 0: most work
@@ -670,6 +680,53 @@ __global__ void reduce_kernel(const float* __restrict__ partial, int64_t ldp, in
     score[j] = acc ? score[j] + v : v;
 }
 
+// The same over the L layers of an all-layer launch, in two kernels so that
+// no thread waits on a chain of L * P loads.  First, for every (token, layer)
+// at once, the layer's head sum formed exactly as reduce_kernel forms it,
+// written over the layer's partial row 0 (each thread reads and writes only
+// its own token's column)...
+__global__ void layer_headsum_kernel(float* __restrict__ partial, int64_t ldp, int P,
+                                     int64_t n) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n) return;
+    float* pl = partial + (int64_t)blockIdx.y * P * ldp;
+    float v = 0.0f;
+    int p = 0;
+    for (; p + 8 <= P; p += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = pl[(int64_t)(p + u) * ldp + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += x[u];
+    }
+    for (; p < P; ++p) v += pl[(int64_t)p * ldp + j];
+    pl[j] = v;
+}
+
+// ...then the layers' sums added to the score in layer order, as a call of
+// reduce_kernel per layer (accumulating from the second layer on) adds them,
+// so the result is bit-identical to scoring the layers one call at a time.
+// ldl = P * ldp is the distance between two layers' row 0.
+__global__ void layer_total_kernel(const float* __restrict__ partial, int64_t ldl, int64_t n,
+                                   int L, float* __restrict__ score, int acc) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n) return;
+    float s = acc ? score[j] : 0.0f;
+    int l = 0;
+    for (; l + 8 <= L; l += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = partial[(int64_t)(l + u) * ldl + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s = (l + u == 0 && !acc) ? x[u] : s + x[u];
+    }
+    for (; l < L; ++l) {
+        const float x = partial[(int64_t)l * ldl + j];
+        s = (l == 0 && !acc) ? x : s + x;
+    }
+    score[j] = s;
+}
+
 // Pass-1 workgroup shape: W heads of a GQA group (the largest of 4, 2, 1
 // that divides R = Hq/Hkv) times QW = 4/W blocks of 64 queries, so always
 // four wavefronts, one per SIMD, and two workgroups per CU.  (Taking W = R
@@ -688,11 +745,11 @@ constexpr int stage_rows() { return D == 256 ? 32 : kStageKeys; }
 
 template <int D, int W>
 hipError_t launch_rowlse_t(const Dims& s, const void* q, const void* k, float* lse2,
-                           hipStream_t st) {
+                           hipStream_t st, int layers) {
     constexpr int QW = rowlse_qblocks(W);
     constexpr int KS = stage_rows<D>();
     const int64_t QB = 64 * QW;
-    const dim3 grid((unsigned)(s.Hq / W), (unsigned)((s.n + QB - 1) / QB));
+    const dim3 grid((unsigned)(s.Hq / W), (unsigned)((s.n + QB - 1) / QB), (unsigned)layers);
     const float c2 = kLog2e / sqrtf((float)s.d);
     const size_t lds = (size_t)3 * KS * (D + 8) * 2;
     hipLaunchKernelGGL((rowlse_kernel<D, W, QW, KS>), grid, dim3(W * QW * 64), lds, st,
@@ -702,21 +759,21 @@ hipError_t launch_rowlse_t(const Dims& s, const void* q, const void* k, float* l
 
 template <int D>
 hipError_t launch_rowlse_d(const Dims& s, const void* q, const void* k, float* lse2,
-                           hipStream_t st) {
+                           hipStream_t st, int layers) {
     switch (rowlse_heads(s.Hq / s.Hkv)) {
-        case 1: return launch_rowlse_t<D, 1>(s, q, k, lse2, st);
-        case 2: return launch_rowlse_t<D, 2>(s, q, k, lse2, st);
-        case 4: return launch_rowlse_t<D, 4>(s, q, k, lse2, st);
+        case 1: return launch_rowlse_t<D, 1>(s, q, k, lse2, st, layers);
+        case 2: return launch_rowlse_t<D, 2>(s, q, k, lse2, st, layers);
+        case 4: return launch_rowlse_t<D, 4>(s, q, k, lse2, st, layers);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int D>
 hipError_t launch_colsum_d(const Dims& s, const void* q, const void* k, const float* lse2,
-                           float* partial, hipStream_t st) {
+                           float* partial, hipStream_t st, int layers) {
     constexpr int QS = stage_rows<D>();
     const int64_t KB = (int64_t)kColKeys * kColWaves;
-    const dim3 grid((unsigned)s.Hq, (unsigned)((s.n + KB - 1) / KB));
+    const dim3 grid((unsigned)s.Hq, (unsigned)((s.n + KB - 1) / KB), (unsigned)layers);
     const float c2 = kLog2e / sqrtf((float)s.d);
     const size_t lds = (size_t)3 * QS * (D + 8) * 2 + (size_t)3 * QS * 4;
     hipLaunchKernelGGL((colsum_kernel<D, kColWaves, QS>), grid, dim3(kColWaves * 64), lds, st,
@@ -730,21 +787,21 @@ hipError_t launch_colsum_d(const Dims& s, const void* q, const void* k, const fl
 int64_t padded_tokens(int64_t n) { return (n + kColKeys - 1) / kColKeys * kColKeys; }
 
 hipError_t launch_rowlse(const Dims& s, const void* q, const void* k, float* lse2,
-                         hipStream_t st) {
+                         hipStream_t st, int layers) {
     switch (s.d) {
-        case 64: return launch_rowlse_d<64>(s, q, k, lse2, st);
-        case 128: return launch_rowlse_d<128>(s, q, k, lse2, st);
-        case 256: return launch_rowlse_d<256>(s, q, k, lse2, st);
+        case 64: return launch_rowlse_d<64>(s, q, k, lse2, st, layers);
+        case 128: return launch_rowlse_d<128>(s, q, k, lse2, st, layers);
+        case 256: return launch_rowlse_d<256>(s, q, k, lse2, st, layers);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_colsum(const Dims& s, const void* q, const void* k, const float* lse2,
-                         float* partial, hipStream_t st) {
+                         float* partial, hipStream_t st, int layers) {
     switch (s.d) {
-        case 64: return launch_colsum_d<64>(s, q, k, lse2, partial, st);
-        case 128: return launch_colsum_d<128>(s, q, k, lse2, partial, st);
-        case 256: return launch_colsum_d<256>(s, q, k, lse2, partial, st);
+        case 64: return launch_colsum_d<64>(s, q, k, lse2, partial, st, layers);
+        case 128: return launch_colsum_d<128>(s, q, k, lse2, partial, st, layers);
+        case 256: return launch_colsum_d<256>(s, q, k, lse2, partial, st, layers);
         default: return hipErrorInvalidValue;
     }
 }
@@ -754,6 +811,17 @@ hipError_t launch_reduce(const Dims& s, const float* partial, float* score, int 
     const unsigned blocks = (unsigned)((s.n + 255) / 256);
     hipLaunchKernelGGL(reduce_kernel, dim3(blocks), dim3(256), 0, st, partial,
                        padded_tokens(s.n), s.Hq, s.n, score, acc);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_layers(const Dims& s, float* partial, float* score, int acc,
+                                hipStream_t st, int layers) {
+    const unsigned blocks = (unsigned)((s.n + 255) / 256);
+    const int64_t ldp = padded_tokens(s.n);
+    hipLaunchKernelGGL(layer_headsum_kernel, dim3(blocks, (unsigned)layers), dim3(256), 0, st,
+                       partial, ldp, s.Hq, s.n);
+    hipLaunchKernelGGL(layer_total_kernel, dim3(blocks), dim3(256), 0, st,
+                       (const float*)partial, (int64_t)s.Hq * ldp, s.n, layers, score, acc);
     return hipGetLastError();
 }
 

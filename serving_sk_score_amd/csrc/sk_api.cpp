@@ -257,6 +257,67 @@ sk_status sk_score_colsum(const sk_shape* shape, int64_t n, const void* q, const
                   "reduce");
 }
 
+// ---- all layers per launch
+
+static sk_status check_layers(const sk_shape* shape) {
+    if (shape->n_layers > 65535)
+        return fail(SK_E_UNSUPPORTED, "all-layer score: n_layers %d above 65535",
+                    shape->n_layers);
+    return SK_OK;
+}
+
+size_t sk_score_colsum_layers_workspace_bytes(const sk_shape* shape, int64_t n) {
+    if (check_shape(shape) || check_tokens(n) || shape->n_layers > 65535) return 0;
+    return (size_t)shape->n_layers * partial_bytes(shape, n);
+}
+
+size_t sk_score_layers_workspace_bytes(const sk_shape* shape, int64_t n) {
+    if (check_shape(shape) || check_tokens(n) || shape->n_layers > 65535) return 0;
+    return (size_t)shape->n_layers * (lse_bytes(shape, n) + partial_bytes(shape, n));
+}
+
+sk_status sk_score_rowlse_layers(const sk_shape* shape, int64_t n, const void* q,
+                                 const void* k, float* lse, void* stream) {
+    if (sk_status st = check_score_io(shape, n, q, k)) return st;
+    if (sk_status st = check_layers(shape)) return st;
+    if (n > 0 && !lse) return fail(SK_E_ARG, "lse must be non-NULL");
+    if (!aligned(lse, 4)) return fail(SK_E_ARG, "lse must be 4-byte aligned");
+    if (n == 0) return ok();
+    (void)hipGetLastError();
+    return device(sk::launch_rowlse(dims(shape, n), q, k, lse, (hipStream_t)stream,
+                                    shape->n_layers),
+                  "rowlse");
+}
+
+// lse [L][Hq][n] (dense per layer) -> partial [L][Hq][n_pad] -> score
+static sk_status run_colsum_layers(const sk_shape* shape, int64_t n, const void* q,
+                                   const void* k, const float* lse, float* score,
+                                   int32_t accumulate, float* partial, hipStream_t st) {
+    const sk::Dims d = dims(shape, n);
+    hipError_t e = sk::launch_colsum(d, q, k, lse, partial, st, shape->n_layers);
+    if (e != hipSuccess) return device(e, "colsum");
+    return device(sk::launch_reduce_layers(d, partial, score, accumulate, st, shape->n_layers),
+                  "reduce");
+}
+
+sk_status sk_score_colsum_layers(const sk_shape* shape, int64_t n, const void* q,
+                                 const void* k, const float* lse, float* score,
+                                 int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+    if (sk_status st = check_score_io(shape, n, q, k)) return st;
+    if (sk_status st = check_layers(shape)) return st;
+    if (n > 0 && (!lse || !score)) return fail(SK_E_ARG, "lse and score must be non-NULL");
+    if (!aligned(lse, 4) || !aligned(score, 4)) return fail(SK_E_ARG, "lse and score must be 4-byte aligned");
+    if (accumulate != 0 && accumulate != 1) return fail(SK_E_ARG, "accumulate must be 0 or 1");
+    if (n == 0) return ok();
+    const size_t need = sk_score_colsum_layers_workspace_bytes(shape, n);
+    if (!ws || ws_bytes < need)
+        return fail(SK_E_WORKSPACE, "colsum workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");
+    (void)hipGetLastError();
+    return run_colsum_layers(shape, n, q, k, lse, score, accumulate, (float*)ws,
+                             (hipStream_t)stream);
+}
+
 static sk_status check_score_call(const sk_shape* shape, int64_t n, const void* q,
                                    const void* k, const float* score, int32_t accumulate) {
     if (sk_status st = check_score_io(shape, n, q, k)) return st;
@@ -309,6 +370,26 @@ sk_status sk_score_noalloc(const sk_shape* shape, int64_t n, const void* q, cons
     if (e != hipSuccess) return device(e, "score scratch lookup");
     if (have < need) return fail(SK_E_WORKSPACE, "score scratch holds %zu bytes", have);
     return run_score(shape, n, q, k, score, accumulate, ws, stream);
+}
+
+sk_status sk_score_layers(const sk_shape* shape, int64_t n, const void* q, const void* k,
+                          float* score, int32_t accumulate, void* ws, size_t ws_bytes,
+                          void* stream) {
+    if (sk_status st = check_score_call(shape, n, q, k, score, accumulate)) return st;
+    if (sk_status st = check_layers(shape)) return st;
+    if (n == 0) return ok();
+    const size_t need = sk_score_layers_workspace_bytes(shape, n);
+    if (!ws || ws_bytes < need)
+        return fail(SK_E_WORKSPACE, "score workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");
+    // lse [L][Hq][n] (dense), then the partials from an aligned offset
+    float* lse = (float*)ws;
+    float* partial = (float*)((char*)ws + (size_t)shape->n_layers * lse_bytes(shape, n));
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipError_t e = sk::launch_rowlse(dims(shape, n), q, k, lse, st, shape->n_layers);
+    if (e != hipSuccess) return device(e, "rowlse");
+    return run_colsum_layers(shape, n, q, k, lse, score, accumulate, partial, st);
 }
 
 sk_status sk_recency_weight(int64_t n, double lambda, const float* in, float* out,

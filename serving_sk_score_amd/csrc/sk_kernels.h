@@ -20,16 +20,23 @@ struct TierSeg {
     int64_t off_scale; // byte offset of the scale segment (int tiers)
 };
 
-// score pass 1: lse fp32 [Hq][n], base-2 log of the causal softmax denominator
+// score pass 1: lse fp32 [Hq][n], base-2 log of the causal softmax
+// denominator; with layers > 1, q [layers][n][Hq][d], k [layers][n][Hkv][d]
+// and lse [layers][Hq][n], all layers in one launch
 hipError_t launch_rowlse(const Dims& s, const void* q, const void* k, float* lse,
-                         hipStream_t st);
+                         hipStream_t st, int layers = 1);
 // score pass 2: per-query-head column sums, partial fp32 [Hq][n_pad],
-// n_pad = padded_tokens(n)
+// n_pad = padded_tokens(n) (with layers > 1: [layers][Hq][n_pad])
 hipError_t launch_colsum(const Dims& s, const void* q, const void* k, const float* lse,
-                         float* partial, hipStream_t st);
+                         float* partial, hipStream_t st, int layers = 1);
 // score[j] = (acc ? score[j] : 0) + sum_h partial[h][j], h in order
 hipError_t launch_reduce(const Dims& s, const float* partial, float* score, int acc,
                          hipStream_t st);
+// the same for each of `layers` partial blocks in layer order, as one call of
+// launch_reduce per layer (accumulating from the second on) would; row 0 of
+// each layer's block is overwritten with that layer's head sum
+hipError_t launch_reduce_layers(const Dims& s, float* partial, float* score, int acc,
+                                hipStream_t st, int layers);
 int64_t padded_tokens(int64_t n);
 // Device address and size of the static score workspace on the current
 // device (looked up once per device).

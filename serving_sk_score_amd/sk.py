@@ -26,7 +26,9 @@ EXPORTS = [
     "sk_assign_tiers", "sk_pack", "sk_unpack", "sk_status_string", "sk_last_error",
     "sk_layout_version", "sk_recency_weight", "sk_score_kvnorm", "sk_upgrade_bytes",
     "sk_upgrade_pack", "sk_upgrade_unpack", "sk_balanced_keys", "sk_decode_workspace_bytes",
-    "sk_decode_attention", "sk_score_noalloc",
+    "sk_decode_attention", "sk_score_noalloc", "sk_score_layers_workspace_bytes",
+    "sk_score_layers", "sk_score_rowlse_layers", "sk_score_colsum_layers_workspace_bytes",
+    "sk_score_colsum_layers",
 ]
 
 SCORE_SCRATCH_BYTES = 32 << 20   # SK_SCORE_SCRATCH_BYTES
@@ -119,6 +121,11 @@ def bind(path):
         "sk_score_rowlse": (i32, [P(_Shape), i64, vp, vp, vp, vp]),
         "sk_score_colsum_workspace_bytes": (sz, [P(_Shape), i64]),
         "sk_score_colsum": (i32, [P(_Shape), i64, vp, vp, vp, vp, i32, vp, sz, vp]),
+        "sk_score_layers_workspace_bytes": (sz, [P(_Shape), i64]),
+        "sk_score_layers": (i32, [P(_Shape), i64, vp, vp, vp, i32, vp, sz, vp]),
+        "sk_score_rowlse_layers": (i32, [P(_Shape), i64, vp, vp, vp, vp]),
+        "sk_score_colsum_layers_workspace_bytes": (sz, [P(_Shape), i64]),
+        "sk_score_colsum_layers": (i32, [P(_Shape), i64, vp, vp, vp, vp, i32, vp, sz, vp]),
         "sk_assign_workspace_bytes": (sz, [i64]),
         "sk_assign_tiers": (i32, [P(_Policy), P(_Plan), vp, vp, vp, vp, sz, vp]),
         "sk_pack": (i32, [P(_Shape), P(_Plan), vp, vp, vp, vp, vp, vp]),
@@ -251,6 +258,59 @@ def score_colsum(shape: Shape, q, k, lse, out, accumulate=False, ws=None):
     _check(lib().sk_score_colsum(ctypes.byref(shape.c()), n, _ptr(q), _ptr(k), _ptr(lse),
                                  _ptr(out), int(bool(accumulate)), _ptr(ws), ws.numel(),
                                  _stream(q)))
+    return out
+
+
+def score_layers_workspace_bytes(shape: Shape, n: int) -> int:
+    return int(lib().sk_score_layers_workspace_bytes(ctypes.byref(shape.c()), n))
+
+
+def colsum_layers_workspace_bytes(shape: Shape, n: int) -> int:
+    return int(lib().sk_score_colsum_layers_workspace_bytes(ctypes.byref(shape.c()), n))
+
+
+def _qk_layers(shape, q, k):
+    n = q.shape[1] if q.dim() == 4 else -1
+    L = shape.n_layers
+    _need(q, "q", torch.float16, shape=(L, n, shape.n_q_heads, shape.head_dim))
+    _need(k, "k", torch.float16, shape=(L, n, shape.n_kv_heads, shape.head_dim))
+    return n
+
+
+def score_layers(shape: Shape, q, k, out, accumulate=False, ws=None):
+    """Every layer's column sums into out (fp32 [n]) with one launch per pass;
+    q fp16 [L][n][Hq][d], k fp16 [L][n][Hkv][d]."""
+    n = _qk_layers(shape, q, k)
+    _need(out, "score", torch.float32, shape=(n,))
+    need = score_layers_workspace_bytes(shape, n)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(ws, "ws", torch.uint8, numel=need)
+    _check(lib().sk_score_layers(ctypes.byref(shape.c()), n, _ptr(q), _ptr(k), _ptr(out),
+                                 int(bool(accumulate)), _ptr(ws), ws.numel(), _stream(q)))
+    return out
+
+
+def score_rowlse_layers(shape: Shape, q, k, lse):
+    """lse fp32 [L][Hq][n] of every layer, one launch."""
+    n = _qk_layers(shape, q, k)
+    _need(lse, "lse", torch.float32, shape=(shape.n_layers, shape.n_q_heads, n))
+    _check(lib().sk_score_rowlse_layers(ctypes.byref(shape.c()), n, _ptr(q), _ptr(k),
+                                        _ptr(lse), _stream(q)))
+    return lse
+
+
+def score_colsum_layers(shape: Shape, q, k, lse, out, accumulate=False, ws=None):
+    n = _qk_layers(shape, q, k)
+    _need(lse, "lse", torch.float32, shape=(shape.n_layers, shape.n_q_heads, n))
+    _need(out, "score", torch.float32, shape=(n,))
+    need = colsum_layers_workspace_bytes(shape, n)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(ws, "ws", torch.uint8, numel=need)
+    _check(lib().sk_score_colsum_layers(ctypes.byref(shape.c()), n, _ptr(q), _ptr(k),
+                                        _ptr(lse), _ptr(out), int(bool(accumulate)), _ptr(ws),
+                                        ws.numel(), _stream(q)))
     return out
 
 

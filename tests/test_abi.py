@@ -151,6 +151,28 @@ def test_call_validation_without_device():
     # empty request: OK and nothing touched even with NULL buffers
     assert lib.sk_score(B(shape), 0, None, None, None, 0, None, 0, None) == sk.SK_OK
     assert lib.sk_score_rowlse(B(shape), 0, None, None, None, None) == sk.SK_OK
+    # all-layer score: the same argument rules, an L-fold workspace, and a
+    # layer count the launch grid cannot hold is refused
+    lneed = lib.sk_score_layers_workspace_bytes(B(shape), 100)
+    assert lneed == 2 * need
+    assert lib.sk_score_colsum_layers_workspace_bytes(B(shape), 100) == \
+        2 * lib.sk_score_colsum_workspace_bytes(B(shape), 100)
+    assert lib.sk_score_layers(B(shape), 100, None, FAKE, FAKE, 0, FAKE, lneed, None) == sk.SK_E_ARG
+    assert lib.sk_score_layers(B(shape), 100, FAKE, FAKE, FAKE, 2, FAKE, lneed, None) == sk.SK_E_ARG
+    assert lib.sk_score_layers(B(shape), 100, FAKE, FAKE, FAKE, 0, FAKE, lneed - 1, None) == sk.SK_E_WORKSPACE
+    assert lib.sk_score_layers(B(shape), 100, FAKE, FAKE, FAKE, 0, FAKE_MIS, lneed, None) == sk.SK_E_ARG
+    assert lib.sk_score_layers(B(bad_shape), 100, FAKE, FAKE, FAKE, 0, FAKE, lneed, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_score_rowlse_layers(B(shape), 100, FAKE, FAKE, None, None) == sk.SK_E_ARG
+    assert lib.sk_score_rowlse_layers(B(shape), big, FAKE, FAKE, FAKE, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_score_colsum_layers(B(shape), 100, FAKE, FAKE, FAKE, FAKE, 0, None, 0, None) == sk.SK_E_WORKSPACE
+    assert lib.sk_score_colsum_layers(B(shape), 100, FAKE, FAKE, None, FAKE, 0, FAKE, lneed, None) == sk.SK_E_ARG
+    deep, _ = _c((65536, 4, 2, 64))
+    assert lib.sk_score_layers_workspace_bytes(B(deep), 100) == 0
+    assert lib.sk_score_layers(B(deep), 100, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_score_rowlse_layers(B(deep), 100, FAKE, FAKE, FAKE, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_score_layers(B(shape), 0, None, None, None, 0, None, 0, None) == sk.SK_OK
+    assert lib.sk_score_rowlse_layers(B(shape), 0, None, None, None, None) == sk.SK_OK
+    assert lib.sk_score_colsum_layers(B(shape), 0, None, None, None, None, 0, None, 0, None) == sk.SK_OK
     # assign: plan / policy disagreement, NULLs
     other = sk.Policy(101, 4, 1, 0.5).c()
     assert lib.sk_assign_tiers(B(other), B(pc), FAKE, FAKE, FAKE, None, 0, None) == sk.SK_E_ARG

@@ -108,6 +108,49 @@ def test_rowlse_and_colsum_entry_points():
     _close(out2.cpu().numpy().astype(np.float64), OS.layer_score(q2, k2), "colsum odd n")
 
 
+@pytest.mark.parametrize("seed,L,n,Hq,Hkv,d,acc", [
+    (40, 3, 300, 4, 2, 64, 0), (41, 2, 777, 7, 1, 128, 1), (42, 3, 257, 16, 2, 256, 0),
+    (43, 4, 450, 8, 2, 128, 1), (44, 2, 1, 4, 2, 128, 0), (45, 5, 129, 6, 2, 64, 0),
+])
+def test_all_layer_launch_matches_per_layer_calls(seed, L, n, Hq, Hkv, d, acc):
+    """One launch per pass over every layer gives bit for bit what a call per
+    layer gives (accumulating from the second layer on), and its lse rows are
+    those of the per-layer row pass; the sum over layers meets the oracle."""
+    say("all-layer score", dict(L=L, n=n, Hq=Hq, Hkv=Hkv, d=d, acc=acc))
+    qs, ks = zip(*(_rand(seed * 10 + layer, n, Hq, Hkv, d) for layer in range(L)))
+    Q, Kt = to_dev(np.stack(qs)), to_dev(np.stack(ks))
+    r = np.random.default_rng(seed)
+    init = r.uniform(0.0, 4.0, n).astype(np.float32)
+    s1 = sk.Shape(1, Hq, Hkv, d)
+    sL = sk.Shape(L, Hq, Hkv, d)
+    want = torch.from_numpy(init).cuda()
+    for layer in range(L):
+        sk.score(s1, Q[layer], Kt[layer], want, accumulate=bool(acc or layer > 0))
+    lse1 = torch.empty((L, Hq, n), dtype=torch.float32, device="cuda")
+    for layer in range(L):
+        sk.score_rowlse(s1, Q[layer], Kt[layer], lse1[layer])
+    got = Guarded(4 * n)
+    out = got.as_(torch.float32, (n,))
+    out.copy_(torch.from_numpy(init))
+    sk.score_layers(sL, Q, Kt, out, accumulate=bool(acc))
+    lse = Guarded(4 * L * Hq * n)
+    lseL = lse.as_(torch.float32, (L, Hq, n))
+    sk.score_rowlse_layers(sL, Q, Kt, lseL)
+    out2 = torch.from_numpy(init).cuda()
+    sk.score_colsum_layers(sL, Q, Kt, lseL, out2, accumulate=bool(acc))
+    torch.cuda.synchronize()
+    got.check()
+    lse.check()
+    w = want.cpu().numpy()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), w.view(np.uint32))
+    assert np.array_equal(out2.cpu().numpy().view(np.uint32), w.view(np.uint32))
+    assert np.array_equal(lseL.cpu().numpy().view(np.uint32), lse1.cpu().numpy().view(np.uint32))
+    ref = sum(OS.layer_score(qs[layer], ks[layer]) for layer in range(L))
+    if acc:
+        ref = ref + init.astype(np.float64)
+    _close(out.cpu().numpy().astype(np.float64), ref, "all layers")
+
+
 def test_full_size_mistral_layer():
     """The benchmark's launch configuration, one whole layer against the oracle."""
     cfg = get_config("mistral7b")
