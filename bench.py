@@ -331,7 +331,16 @@ def run_batched(cfg, args, dev, torch, sk):
         tp, tu = pm.sum() * 1e-3 / K_, um.sum() * 1e-3 / K_
         pb = sum(pbytes(b, r) for r in range(R))
         ub = sum(ubytes(b, r) for r in range(R))
+        # per request, over all steps: launch r of each step
+        pms = pm.reshape(K_, R).mean(axis=0)
+        ums = um.reshape(K_, R).mean(axis=0)
+        per_req_b = [{"n": lengths[r], "pack_ms": round(float(pms[r]), 4),
+                      "pack_frac": round(pbytes(b, r) / (pms[r] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "unpack_paged_ms": round(float(ums[r]), 4),
+                      "unpack_paged_frac": round(ubytes(b, r) / (ums[r] * 1e-3) / 1e9
+                                                 / HBM_PEAK_GBS, 4)} for r in range(R)]
         per_budget[str(b)] = {
+            "per_request": per_req_b,
             "payload_bytes": sum(plans[b][r].payload_bytes for r in range(R)),
             "counts": [int(sum(getattr(plans[b][r], f) for r in range(R)))
                        for f in ("n16", "n8", "n4")],
