@@ -74,3 +74,54 @@ def test_every_column_longest_batched_request():
     k = gen.keys(cfg, layer, n, request=r)
     q = gen.queries(cfg, layer, n, request=r, k=k)
     _group_check("batched_mix", q, k, 0, f"batched request {r} (n={n}) layer {layer}")
+
+
+@pytest.mark.parametrize("name", ["mistral7b", "qwen25_7b_2tier", "gemma2_9b", "batched_mix"])
+def test_all_layer_launch_full_size(name):
+    """The launch configuration the benchmark times: every layer of a request
+    at full size in one launch per pass (sk_score_rowlse_layers +
+    sk_score_colsum_layers, and sk_score_layers), on the inputs the benchmark
+    draws on the device.  The score must be bit for bit that of one sk_score
+    call per layer, accumulating from the second layer on - the per-layer
+    path the tests above and the per-layer full-size tests compare with the
+    oracle - and meet the row-stochastic invariant sum_j A_j = L * H_q * n.
+    For the batched mix, its longest request."""
+    from workloads import gen_device as gd
+    cfg = get_config(name)
+    L, Hq, Hkv, d = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim
+    if cfg.requests:
+        lengths = gen.request_lengths(cfg)
+        r = int(np.argmax(lengths))
+        n = lengths[r]
+    else:
+        r, n = 0, cfg.tokens
+    say("all-layer launch", name, dict(L=L, n=n, Hq=Hq, Hkv=Hkv, d=d))
+    Q = torch.empty((L, n, Hq, d), dtype=torch.float16, device="cuda")
+    K = torch.empty((L, n, Hkv, d), dtype=torch.float16, device="cuda")
+    for layer in range(L):
+        gd.keys(cfg, layer, n, r, out=K[layer])
+        gd.queries(cfg, layer, n, r, k=K[layer], out=Q[layer])
+    s1 = sk.Shape(1, Hq, Hkv, d)
+    sL = sk.Shape(L, Hq, Hkv, d)
+    want = torch.empty(n, dtype=torch.float32, device="cuda")
+    for layer in range(L):
+        sk.score(s1, Q[layer], K[layer], want, accumulate=layer > 0)
+    lse = Guarded(4 * L * Hq * n)
+    out = Guarded(4 * n)
+    sk.score_rowlse_layers(sL, Q, K, lse.as_(torch.float32, (L, Hq, n)))
+    sk.score_colsum_layers(sL, Q, K, lse.as_(torch.float32, (L, Hq, n)),
+                           out.as_(torch.float32, (n,)))
+    one = torch.empty(n, dtype=torch.float32, device="cuda")
+    sk.score_layers(sL, Q, K, one)
+    torch.cuda.synchronize()
+    lse.check()
+    out.check()
+    w = want.cpu().numpy()
+    got = out.as_(torch.float32, (n,)).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), w.view(np.uint32)), "two-call all-layer score"
+    assert np.array_equal(one.cpu().numpy().view(np.uint32), w.view(np.uint32)), "sk_score_layers"
+    g64 = got.astype(np.float64)
+    assert np.all(g64 > 0) and np.all(np.isfinite(g64))
+    assert abs(g64.sum() - L * Hq * n) <= 1e-4 * L * Hq * n, "row-stochastic invariant"
+    del Q, K
+    torch.cuda.empty_cache()
