@@ -203,11 +203,14 @@ sk_status sk_score_colsum(const sk_shape* shape, int64_t n_tokens,
                           float* score, int32_t accumulate,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* All layers in one launch per pass: the same score as calling sk_score once
- * per layer l = 0 .. n_layers - 1 with accumulate = (l > 0 || accumulate),
- * bit for bit, for a caller that holds every layer's queries and keys.  One
- * launch per pass instead of one per layer removes the per-launch fill and
- * drain (about 30 us each), which is a tenth of a layer's time at 8K tokens.
+/* All layers in one launch per pass: the importance score summed over the
+ * layers (SpectrumKV paper §4.3 "Importance scores", Algorithm 1 "score
+ * tokens"), the same as calling sk_score once per layer l = 0 .. n_layers - 1
+ * with accumulate = (l > 0 || accumulate), bit for bit, for a caller that
+ * holds every layer's queries and keys.  One launch per pass instead of one
+ * per layer removes the per-launch fill and drain (about 30 us each), which
+ * is a tenth of a layer's time at 8K tokens.  sk_score_colsum_layers takes
+ * the lse that sk_score_rowlse_layers wrote for the same q and k.
  *   q     : fp16 [n_layers][n][n_q_heads][head_dim]
  *   k     : fp16 [n_layers][n][n_kv_heads][head_dim] (the layout sk_pack reads)
  *   score : fp32 [n]; overwritten (accumulate = 0) or added to (1)
