@@ -900,7 +900,11 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ par
                                                    int Hq, float* __restrict__ out,
                                                    float* __restrict__ lse) {
     constexpr int CPL = (D + 63) / 64;  // channels per lane
-    constexpr int U = 4;                // chunks whose loads are in flight together
+    // chunks whose loads are in flight together: with 16, the 65 chunk
+    // records of a Qwen- or Gemma-shaped (layer, head) take 5 round trips to
+    // memory instead of 17 (12.0 -> 9.8 us at d = 128, 20.8 -> 16.5 us at
+    // d = 256); the additions keep chunk order, so the result is unchanged
+    constexpr int U = 16;
     const int lane = threadIdx.x;
     const int h = blockIdx.x;
     const int li = blockIdx.y;
