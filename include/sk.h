@@ -219,7 +219,9 @@ sk_status sk_score_colsum(const sk_shape* shape, int64_t n_tokens,
  *   ws    : at least sk_score_layers_workspace_bytes (sk_score_layers) or
  *           sk_score_colsum_layers_workspace_bytes (sk_score_colsum_layers)
  *           bytes, n_layers times the one-layer sizes; scratch between calls.
- * Token limit and errors as sk_score; n_layers must be at most 65535. */
+ * Token limit and errors as sk_score; n_layers must be at most 65535.  A
+ * shape whose all-layer workspace would not fit in size_t gets 0 from the
+ * size queries and SK_E_UNSUPPORTED from the calls. */
 size_t    sk_score_layers_workspace_bytes(const sk_shape* shape, int64_t n_tokens);
 sk_status sk_score_layers(const sk_shape* shape, int64_t n_tokens,
                           const void* q, const void* k, float* score, int32_t accumulate,

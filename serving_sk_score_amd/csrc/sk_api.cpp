@@ -259,27 +259,27 @@ sk_status sk_score_colsum(const sk_shape* shape, int64_t n, const void* q, const
 
 // ---- all layers per launch
 
-static sk_status check_layers(const sk_shape* shape) {
-    if (shape->n_layers > 65535)
-        return fail(SK_E_UNSUPPORTED, "all-layer score: n_layers %d above 65535",
-                    shape->n_layers);
-    return SK_OK;
+// n_layers times a one-layer workspace size, or 0 when the product does not
+// fit in size_t (a shape no device could hold; the calls then refuse it)
+static size_t times_layers(const sk_shape* shape, size_t per_layer) {
+    size_t r;
+    if (__builtin_mul_overflow((size_t)shape->n_layers, per_layer, &r)) return 0;
+    return r;
 }
 
 size_t sk_score_colsum_layers_workspace_bytes(const sk_shape* shape, int64_t n) {
-    if (check_shape(shape) || check_tokens(n) || shape->n_layers > 65535) return 0;
-    return (size_t)shape->n_layers * partial_bytes(shape, n);
+    if (check_shape(shape) || check_tokens(n)) return 0;
+    return times_layers(shape, partial_bytes(shape, n));
 }
 
 size_t sk_score_layers_workspace_bytes(const sk_shape* shape, int64_t n) {
-    if (check_shape(shape) || check_tokens(n) || shape->n_layers > 65535) return 0;
-    return (size_t)shape->n_layers * (lse_bytes(shape, n) + partial_bytes(shape, n));
+    if (check_shape(shape) || check_tokens(n)) return 0;
+    return times_layers(shape, lse_bytes(shape, n) + partial_bytes(shape, n));
 }
 
 sk_status sk_score_rowlse_layers(const sk_shape* shape, int64_t n, const void* q,
                                  const void* k, float* lse, void* stream) {
     if (sk_status st = check_score_io(shape, n, q, k)) return st;
-    if (sk_status st = check_layers(shape)) return st;
     if (n > 0 && !lse) return fail(SK_E_ARG, "lse must be non-NULL");
     if (!aligned(lse, 4)) return fail(SK_E_ARG, "lse must be 4-byte aligned");
     if (n == 0) return ok();
@@ -304,12 +304,12 @@ sk_status sk_score_colsum_layers(const sk_shape* shape, int64_t n, const void* q
                                  const void* k, const float* lse, float* score,
                                  int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
     if (sk_status st = check_score_io(shape, n, q, k)) return st;
-    if (sk_status st = check_layers(shape)) return st;
     if (n > 0 && (!lse || !score)) return fail(SK_E_ARG, "lse and score must be non-NULL");
     if (!aligned(lse, 4) || !aligned(score, 4)) return fail(SK_E_ARG, "lse and score must be 4-byte aligned");
     if (accumulate != 0 && accumulate != 1) return fail(SK_E_ARG, "accumulate must be 0 or 1");
     if (n == 0) return ok();
     const size_t need = sk_score_colsum_layers_workspace_bytes(shape, n);
+    if (need == 0) return fail(SK_E_UNSUPPORTED, "colsum workspace size overflows size_t");
     if (!ws || ws_bytes < need)
         return fail(SK_E_WORKSPACE, "colsum workspace needs %zu bytes, got %zu", need, ws_bytes);
     if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");
@@ -376,9 +376,9 @@ sk_status sk_score_layers(const sk_shape* shape, int64_t n, const void* q, const
                           float* score, int32_t accumulate, void* ws, size_t ws_bytes,
                           void* stream) {
     if (sk_status st = check_score_call(shape, n, q, k, score, accumulate)) return st;
-    if (sk_status st = check_layers(shape)) return st;
     if (n == 0) return ok();
     const size_t need = sk_score_layers_workspace_bytes(shape, n);
+    if (need == 0) return fail(SK_E_UNSUPPORTED, "score workspace size overflows size_t");
     if (!ws || ws_bytes < need)
         return fail(SK_E_WORKSPACE, "score workspace needs %zu bytes, got %zu", need, ws_bytes);
     if (!aligned(ws, 16)) return fail(SK_E_ARG, "workspace must be 16-byte aligned");

@@ -166,6 +166,14 @@ def test_call_validation_without_device():
     assert lib.sk_score_rowlse_layers(B(shape), big, FAKE, FAKE, FAKE, None) == sk.SK_E_UNSUPPORTED
     assert lib.sk_score_colsum_layers(B(shape), 100, FAKE, FAKE, FAKE, FAKE, 0, None, 0, None) == sk.SK_E_WORKSPACE
     assert lib.sk_score_colsum_layers(B(shape), 100, FAKE, FAKE, None, FAKE, 0, FAKE, lneed, None) == sk.SK_E_ARG
+    # a workspace that n_layers times the one-layer size would overflow
+    huge, _ = _c((65535, 16 * (2 ** 27 - 1), 2 ** 27 - 1, 64))
+    assert lib.sk_score_layers_workspace_bytes(B(huge), 4_000_000) == 0
+    assert lib.sk_score_colsum_layers_workspace_bytes(B(huge), 4_000_000) == 0
+    assert lib.sk_score_layers(B(huge), 4_000_000, FAKE, FAKE, FAKE, 0, FAKE, 1 << 62, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_score_colsum_layers(B(huge), 4_000_000, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 62, None) == sk.SK_E_UNSUPPORTED
+    assert b"overflows" in lib.sk_last_error()
+    assert lib.sk_score_workspace_bytes(B(huge), 4_000_000) > 0   # one layer still fits
     deep, _ = _c((65536, 4, 2, 64))
     assert lib.sk_score_layers_workspace_bytes(B(deep), 100) == 0
     assert lib.sk_score_layers(B(deep), 100, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == sk.SK_E_UNSUPPORTED
