@@ -139,8 +139,10 @@ typedef struct {
 } sk_plan;
 
 /* Host only, pure, touches no device.  Returns SK_E_ARG / SK_E_UNSUPPORTED
- * for a bad shape or policy and SK_E_BUDGET when the budget cannot pay every
- * token under the policy's overflow mode (out is then left untouched). */
+ * for a bad shape or policy (SK_E_UNSUPPORTED too when the fp16 KV of the
+ * request, 4 * L * n * H * d bytes, is beyond 2^62, so that every offset
+ * fits int64) and SK_E_BUDGET when the budget cannot pay every token under
+ * the policy's overflow mode (out is then left untouched). */
 sk_status sk_plan_make(const sk_shape* shape, const sk_policy* policy, sk_plan* out);
 
 /* ---------------------------------------------------------------- score --

@@ -49,6 +49,13 @@ sk_status check_shape(const sk_shape* s) {
     return SK_OK;
 }
 
+// Whether the fp16 K and V of n tokens, 4 * L * n * H * d bytes, stay within
+// 2^62: then every payload offset and size (at most twice that) fits int64.
+bool kv_fits(const sk_shape* s, int64_t n) {
+    const __int128 kv = (__int128)4 * s->n_layers * n * s->n_kv_heads * s->head_dim;
+    return kv <= ((__int128)1 << 62);
+}
+
 sk_status check_tokens(int64_t n) {
     if (n < 0 || n >= kMaxTokens) return fail(SK_E_ARG, "n_tokens %lld outside [0, 2^30)", (long long)n);
     return SK_OK;
@@ -137,6 +144,9 @@ sk_status sk_plan_make(const sk_shape* shape, const sk_policy* pol, sk_plan* out
     if (pol->overflow != SK_OVERFLOW_REJECT && pol->overflow != SK_OVERFLOW_DROP &&
         pol->overflow != SK_OVERFLOW_FALLBACK)
         return fail(SK_E_ARG, "overflow must be one of SK_OVERFLOW_*");
+    if (!kv_fits(shape, pol->n_tokens))
+        return fail(SK_E_UNSUPPORTED, "shape: the fp16 KV of %lld tokens is beyond 2^62 bytes",
+                    (long long)pol->n_tokens);
 
     const int64_t n = pol->n_tokens;
     const int64_t S = pol->n_sink < n ? pol->n_sink : n;
@@ -558,7 +568,7 @@ sk_status sk_decode_attention(const sk_shape* shape, const sk_plan* plan, const 
 }
 
 size_t sk_upgrade_bytes(const sk_shape* shape, int64_t m) {
-    if (check_shape(shape) || m < 0 || m >= kMaxTokens) return 0;
+    if (check_shape(shape) || m < 0 || m >= kMaxTokens || !kv_fits(shape, m)) return 0;
     return (size_t)shape->n_layers * (size_t)m * 2 * (size_t)shape->n_kv_heads * 2 *
            (size_t)shape->head_dim;
 }
@@ -568,6 +578,9 @@ static sk_status check_upgrade(const sk_shape* shape, int64_t n, int64_t m,
     if (sk_status st = check_shape(shape)) return st;
     if (sk_status st = check_tokens(n)) return st;
     if (m < 0 || m >= kMaxTokens) return fail(SK_E_ARG, "n_up %lld outside [0, 2^30)", (long long)m);
+    if (!kv_fits(shape, n))
+        return fail(SK_E_UNSUPPORTED, "shape: the fp16 KV of %lld tokens is beyond 2^62 bytes",
+                    (long long)n);
     if (m == 0) return SK_OK;
     if (!tokens || !payload) return fail(SK_E_ARG, "tokens and payload must be non-NULL");
     if (!aligned(tokens, 4)) return fail(SK_E_ARG, "tokens must be 4-byte aligned");

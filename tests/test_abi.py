@@ -241,6 +241,13 @@ def test_call_validation_without_device():
     assert lib.sk_upgrade_unpack(B(shape), 100, FAKE, FAKE, 3, None, None, B(pg_ok), None) == sk.SK_E_ARG
     assert lib.sk_upgrade_unpack(B(shape), 100, FAKE, FAKE, 3, None, None, B(pg), None) == sk.SK_E_ARG
     assert lib.sk_upgrade_unpack(B(shape), 100, None, None, 0, None, None, None, None) == sk.SK_OK
+    # shapes whose fp16 KV would pass 2^62 bytes: no plan, no upgrade size
+    vast, _ = _c((65535, 2 ** 30, 2 ** 26, 256))
+    vp = sk.Policy(1 << 20, 4, 1, 0.5).c()
+    assert lib.sk_plan_make(B(vast), B(vp), B(sk._Plan())) == sk.SK_E_UNSUPPORTED
+    assert b"2^62" in lib.sk_last_error()
+    assert lib.sk_upgrade_bytes(B(vast), 1 << 20) == 0
+    assert lib.sk_upgrade_pack(B(vast), 1 << 20, FAKE, FAKE, FAKE, 3, FAKE, None) == sk.SK_E_UNSUPPORTED
     empty = _plan((2, 4, 2, 64), (0, 4, 1, 0.5))
     assert lib.sk_pack(B(shape), B(empty.c), None, None, None, None, None, None) == sk.SK_OK
     assert lib.sk_unpack(B(shape), B(empty.c), None, None, None, None, None, None) == sk.SK_OK
