@@ -162,7 +162,8 @@ sk_status sk_plan_make(const sk_shape* shape, const sk_policy* policy, sk_plan* 
  * per-query-head partial sums are then added in a fixed order, so the
  * result is deterministic.  The score calls (this one, sk_score_rowlse and
  * sk_score_colsum) take n_tokens <= 4,194,240 (65535 blocks of 64 queries);
- * a longer request returns SK_E_UNSUPPORTED. */
+ * a longer request returns SK_E_UNSUPPORTED, and the workspace queries
+ * return 0 for it. */
 size_t    sk_score_workspace_bytes(const sk_shape* shape, int64_t n_tokens);
 sk_status sk_score(const sk_shape* shape, int64_t n_tokens,
                    const void* q, const void* k, float* score, int32_t accumulate,

@@ -212,19 +212,19 @@ sk_status sk_plan_make(const sk_shape* shape, const sk_policy* pol, sk_plan* out
     return ok();
 }
 
+// The row pass launches one workgroup row per 64 queries (for four heads per
+// workgroup) and a launch grid holds at most 65535 rows.
+constexpr int64_t kMaxScoreTokens = (int64_t)65535 * 64;
+
 size_t sk_score_colsum_workspace_bytes(const sk_shape* shape, int64_t n) {
-    if (check_shape(shape) || check_tokens(n)) return 0;
+    if (check_shape(shape) || check_tokens(n) || n > kMaxScoreTokens) return 0;
     return partial_bytes(shape, n);
 }
 
 size_t sk_score_workspace_bytes(const sk_shape* shape, int64_t n) {
-    if (check_shape(shape) || check_tokens(n)) return 0;
+    if (check_shape(shape) || check_tokens(n) || n > kMaxScoreTokens) return 0;
     return lse_bytes(shape, n) + partial_bytes(shape, n);
 }
-
-// The row pass launches one workgroup row per 64 queries (for four heads per
-// workgroup) and a launch grid holds at most 65535 rows.
-constexpr int64_t kMaxScoreTokens = (int64_t)65535 * 64;
 
 static sk_status check_score_io(const sk_shape* shape, int64_t n, const void* q, const void* k) {
     if (sk_status st = check_shape(shape)) return st;
@@ -278,12 +278,12 @@ static size_t times_layers(const sk_shape* shape, size_t per_layer) {
 }
 
 size_t sk_score_colsum_layers_workspace_bytes(const sk_shape* shape, int64_t n) {
-    if (check_shape(shape) || check_tokens(n)) return 0;
+    if (check_shape(shape) || check_tokens(n) || n > kMaxScoreTokens) return 0;
     return times_layers(shape, partial_bytes(shape, n));
 }
 
 size_t sk_score_layers_workspace_bytes(const sk_shape* shape, int64_t n) {
-    if (check_shape(shape) || check_tokens(n)) return 0;
+    if (check_shape(shape) || check_tokens(n) || n > kMaxScoreTokens) return 0;
     return times_layers(shape, lse_bytes(shape, n) + partial_bytes(shape, n));
 }
 

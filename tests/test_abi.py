@@ -136,6 +136,9 @@ def test_call_validation_without_device():
     big = 65535 * 64 + 1
     assert lib.sk_score_rowlse(B(shape), big, FAKE, FAKE, FAKE, None) == sk.SK_E_UNSUPPORTED
     assert lib.sk_score(B(shape), big, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == sk.SK_E_UNSUPPORTED
+    assert lib.sk_score_workspace_bytes(B(shape), big) == 0
+    assert lib.sk_score_colsum_workspace_bytes(B(shape), big) == 0
+    assert lib.sk_score_workspace_bytes(B(shape), big - 1) > 0
     # allocation-free score: same argument checks, and a request larger than
     # the static scratch is rejected before any device is touched
     assert lib.sk_score_noalloc(B(shape), 100, None, FAKE, FAKE, 0, None) == sk.SK_E_ARG
