@@ -82,6 +82,11 @@ __device__ void find_digit(const uint32_t* hist, uint64_t k, int lane, int* out_
     }
 }
 
+// Steps of 64 tokens per wavefront and round in the slot pass (2 bits of
+// tier per step are kept in one 32-bit register, so at most 16).
+constexpr int kChunk = 16;
+constexpr int kBatch = 8;  // score loads in flight per thread
+
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ score, int64_t n, int64_t sinks, int64_t k1, int64_t k2,
     int64_t k3, int64_t n16, int64_t n8, int64_t n4, uint32_t* __restrict__ map,
@@ -92,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     __shared__ uint64_t krem[NS];
     __shared__ int sel_digit[NS];
     __shared__ uint64_t sel_above[NS];
-    __shared__ uint32_t wcnt[kWaves][4];
+    __shared__ int live[NS];
+    __shared__ uint32_t wtot[kWaves][4];
     __shared__ uint32_t running[4];
 
     const int tid = threadIdx.x;
@@ -108,19 +114,26 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     // cond_s(key) = rank < k_s: false for k_s <= 0, true for k_s >= R, else
     // a radix-selected threshold
     const int64_t ks[NS] = {k1, k2, k3};
-    bool active[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) active[s] = ks[s] >= 1 && ks[s] < R;
     if (tid == 0) {
         for (int s = 0; s < NS; ++s) {
+            live[s] = ks[s] >= 1 && ks[s] < R;
             prefix[s] = 0;
-            krem[s] = (uint64_t)(active[s] ? ks[s] : 1);
+            krem[s] = (uint64_t)(live[s] ? ks[s] : 1);
         }
     }
-    const bool any = active[0] || active[1] || active[2];
+    __syncthreads();
     uint64_t pmask = 0;  // bits of the key fixed so far (uniform)
 
-    for (int p = 0; p < passes && any; ++p) {
+    // A threshold stops being narrowed once its prefix matches a single key:
+    // that key is then the only one with the prefix, so comparing with the
+    // prefix (low bits zero) ranks every key exactly as comparing with the
+    // key itself.  With distinct scores this ends the search within the
+    // score bits, before the index bits.
+    for (int p = 0; p < passes; ++p) {
+        bool active[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) active[s] = live[s] != 0;
+        if (!(active[0] || active[1] || active[2])) break;
         const int shift = 8 * (passes - 1 - p);
         for (int i = tid; i < NS * 256; i += kThreads) (&hist[0][0])[i] = 0;
         __syncthreads();
@@ -133,18 +146,32 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
             run_d[s] = -1;
             run_c[s] = 0;
         }
-        for (int64_t j = sinks + tid; j < n; j += kThreads) {
-            const uint64_t key = make_key(score[j], j, bits);
-            const int dg = (int)((key >> shift) & 0xFFu);
+        // this thread's tokens sinks + tid, + kThreads, ... in that order,
+        // kBatch loads issued before any is used
+        for (int64_t jb = sinks + tid; jb < n; jb += (int64_t)kThreads * kBatch) {
+            float sv[kBatch];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if (active[s] && (key & pmask) == pre[s]) {
-                    if (dg != run_d[s]) {
-                        if (run_c[s]) atomicAdd(&hist[s][run_d[s]], run_c[s]);
-                        run_d[s] = dg;
-                        run_c[s] = 0;
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t j = jb + (int64_t)u * kThreads;
+                sv[u] = j < n ? score[j] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t j = jb + (int64_t)u * kThreads;
+                if (j < n) {
+                    const uint64_t key = make_key(sv[u], j, bits);
+                    const int dg = (int)((key >> shift) & 0xFFu);
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) {
+                        if (active[s] && (key & pmask) == pre[s]) {
+                            if (dg != run_d[s]) {
+                                if (run_c[s]) atomicAdd(&hist[s][run_d[s]], run_c[s]);
+                                run_d[s] = dg;
+                                run_c[s] = 0;
+                            }
+                            ++run_c[s];
+                        }
                     }
-                    ++run_c[s];
                 }
             }
         }
@@ -161,6 +188,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
                 if (!active[s]) continue;
                 prefix[s] |= (uint64_t)sel_digit[s] << shift;
                 krem[s] -= sel_above[s];
+                if (hist[s][sel_digit[s]] == 1u) live[s] = 0;
             }
         }
         pmask |= (uint64_t)0xFFu << shift;
@@ -175,46 +203,84 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         all[s] = ks[s] >= R;
         none[s] = ks[s] <= 0;
     }
+    auto tier_of = [&](int64_t j, float sc) -> int {
+        if (j < sinks) return 0;
+        const uint64_t key = make_key(sc, j, bits);
+        int tier = 3;
+#pragma unroll
+        for (int s = NS - 1; s >= 0; --s)
+            if (!none[s] && (all[s] || key >= K[s])) tier = s;
+        return tier;
+    };
     const uint32_t base[4] = {0u, (uint32_t)n16, (uint32_t)(n16 + n8),
                               (uint32_t)(n16 + n8 + n4)};
     if (tid < 4) running[tid] = 0;
     __syncthreads();
-    for (int64_t t0 = 0; t0 < n; t0 += kThreads) {
-        const int64_t j = t0 + tid;
-        int tier = -1;
-        if (j < n) {
-            if (j < sinks) {
-                tier = 0;
-            } else {
-                const uint64_t key = make_key(score[j], j, bits);
-                tier = 3;
+    // Slots, kThreads * S tokens a round, S = kChunk steps or, in the last
+    // round, as few as the remaining tokens need: wavefront w takes the
+    // contiguous 64 * S tokens from t0 + 64 * S * w, 64 consecutive tokens a
+    // step (coalesced).  A first walk finds every token's tier (2
+    // bits per step, kept in one register) and the wavefront's count per
+    // tier (ballots); one workgroup scan of those counts gives each
+    // wavefront its offsets; a second walk numbers the tokens of each tier
+    // in token order with ballot prefixes and writes map and order.
+    const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
+    for (int64_t t0 = 0; t0 < n;) {
+        const int64_t left = n - t0;
+        const int S = left >= (int64_t)kThreads * kChunk
+                          ? kChunk
+                          : (int)((left + kThreads - 1) / kThreads);
+        const int64_t w0 = t0 + (int64_t)wave * 64 * S + lane;
+        uint32_t packed = 0;
+        uint32_t wc[4] = {0u, 0u, 0u, 0u};
+        for (int b = 0; b < S; b += kBatch) {
+            float sv[kBatch];
 #pragma unroll
-                for (int s = NS - 1; s >= 0; --s)
-                    if (!none[s] && (all[s] || key >= K[s])) tier = s;
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t j = w0 + 64 * (b + u);
+                sv[u] = (b + u < S && j < n) ? score[j] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t j = w0 + 64 * (b + u);
+                const int t = (b + u < S && j < n) ? tier_of(j, sv[u]) : 4;
+                packed |= (uint32_t)(t & 3) << (2 * (b + u));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) wc[q] += (uint32_t)__popcll(__ballot(t == q));
             }
         }
-        uint32_t mypre = 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const unsigned long long b = __ballot(tier == t);
-            if (lane == 0) wcnt[wave][t] = (uint32_t)__popcll(b);
-            if (tier == t) mypre = (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
-        }
+        if (lane < 4) wtot[wave][lane] = wc[lane];
         __syncthreads();
-        if (tier >= 0) {
-            uint32_t off = running[tier];
-            for (int w = 0; w < wave; ++w) off += wcnt[w][tier];
-            const uint32_t slot = off + mypre;
-            map[j] = ((uint32_t)tier << 30) | slot;
-            order[base[tier] + slot] = (uint32_t)j;
+        uint32_t off[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            off[q] = running[q];
+            for (int w = 0; w < wave; ++w) off[q] += wtot[w][q];
+        }
+        for (int i = 0; i < S; ++i) {
+            const int64_t j = w0 + 64 * i;
+            const bool valid = j < n;
+            const int t = (int)((packed >> (2 * i)) & 3u);
+            uint32_t slot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const unsigned long long bq = __ballot(valid && t == q);
+                if (valid && t == q) slot = off[q] + (uint32_t)__popcll(bq & below);
+                off[q] += (uint32_t)__popcll(bq);
+            }
+            if (valid) {
+                map[j] = ((uint32_t)t << 30) | slot;
+                order[base[t] + slot] = (uint32_t)j;
+            }
         }
         __syncthreads();
         if (tid < 4) {
-            uint32_t s = 0;
-            for (int w = 0; w < kWaves; ++w) s += wcnt[w][tid];
-            running[tid] += s;
+            uint32_t tot = 0;
+            for (int w = 0; w < kWaves; ++w) tot += wtot[w][tid];
+            running[tid] += tot;
         }
         __syncthreads();
+        t0 += (int64_t)kThreads * S;
     }
 }
 
