@@ -50,10 +50,28 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
     return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xFFFFu)));
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// The maximum over each aligned group of LPR lanes (8, 16 or 32).  Within a
+// row of 16 lanes it takes four DPP moves, each folded into its v_max: lane ^
+// 1 and lane ^ 2 within a quad, then lane 7 - i of the 8-lane half row and
+// lane 15 - i of the row, so that every lane meets every other lane of its
+// group; 32-lane groups add one swizzle (lane ^ 16).  Max is exact in any
+// order, so the result is that of any other reduction.
 template <int LPR>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "groups of 8, 16 or 32 lanes");
+    v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+    v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+    v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+    if constexpr (LPR >= 16) v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+    if constexpr (LPR >= 32)  // bitmask swizzle: and 0x1F, xor 0x10
+        v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(
+                                                   __builtin_bit_cast(int, v), 0x401F)));
     return v;
 }
 
