@@ -15,11 +15,13 @@
 // tie, a lower index; for non-negative floats the IEEE bit pattern is
 // monotone.  The thresholds strictly inside (0, R) are found with one
 // MSB-first radix select (8-bit digits, LDS histograms, one workgroup) - each
-// pass narrows the prefixes of all of them at once.  A token is fp16 iff
+// pass narrows the prefixes of all of them at once, and a threshold whose
+// prefix already matches a single key is settled.  A token is fp16 iff
 // key >= K_k1, else int8 iff key >= K_k2, else int4 iff key >= K_k3, else
 // dropped.  Slots (positions among the same tier in token order) come from
-// wavefront ballots and a workgroup prefix over 1024-token tiles; order[] is
-// the inverse permutation, dropped tokens last.
+// per-wavefront tier counts (ballots), one workgroup scan of them per round
+// and ballot prefixes within each 64-token step; order[] is the inverse
+// permutation, dropped tokens last.
 //
 // Histogram contention: the top digits of nearby scores coincide, so every
 // thread first merges runs of equal digits in registers and issues one LDS
