@@ -866,6 +866,24 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(PartialArgs a) {
     partial_mfma<D, TIER, P4, false>(a, a.tier[TIER], blockIdx.x, blockIdx.y, vt, pt);
 }
 
+// The fp16 and int4 tiers in one launch when both are a few chunks (sinks
+// and a handful of int4 tokens at b = 0.5): blocks below the fp16 tier's
+// chunk count run that tier, the others the int4 tier.  At d = 128 both
+// use the matrix-core body with the same LDS; one launch instead of two
+// saves the second launch's fill and drain (about 5 us).
+constexpr int64_t kTinyChunks = 4;
+
+template <int D, bool P4>
+__global__ __launch_bounds__(64) void decode_mfma_tiny_kernel(PartialArgs a, int chunks0) {
+    static_assert(!half_v<D, 0, P4>() && !half_v<D, 2, P4>(), "same LDS for both tiers");
+    __shared__ __align__(16) _Float16 vt[32 * mfma_vt_pitch<D>()];
+    __shared__ __align__(16) _Float16 pt[P4 ? 4 * 64 : 4];
+    if ((int)blockIdx.x < chunks0)
+        partial_mfma<D, 0, P4, false>(a, a.tier[0], blockIdx.x, blockIdx.y, vt, pt);
+    else
+        partial_mfma<D, 2, P4, false>(a, a.tier[2], blockIdx.x - chunks0, blockIdx.y, vt, pt);
+}
+
 // KV heads (wavefronts) of a workgroup of the one-per-head form: eight keep
 // the register budget of two wavefronts per SIMD.
 constexpr int kWgMaxHeads = 8;
@@ -1008,8 +1026,25 @@ template <int D>
 hipError_t launch_all(const PartialArgs& a, int nl, int GM, float* out, float* lse,
                       hipStream_t st) {
     hipError_t e = launch_tier<D, 1>(a, nl, GM, st);
-    if (e == hipSuccess) e = launch_tier<D, 2>(a, nl, GM, st);
-    if (e == hipSuccess) e = launch_tier<D, 0>(a, nl, GM, st);
+    const int64_t ch0 = a.cend[0] - a.tier[0].chunk_base;
+    const int64_t ch2 = a.cend[2] - a.tier[2].chunk_base;
+    bool tiny = false;
+    if constexpr (D == 128) tiny = ch0 > 0 && ch2 > 0 && ch0 + ch2 <= kTinyChunks;
+    if (tiny) {
+        if constexpr (D == 128) {
+            const dim3 grid((unsigned)(ch0 + ch2), (unsigned)a.H, (unsigned)nl);
+            if (e == hipSuccess) {
+                if (GM <= 4)
+                    decode_mfma_tiny_kernel<D, true><<<grid, 64, 0, st>>>(a, (int)ch0);
+                else
+                    decode_mfma_tiny_kernel<D, false><<<grid, 64, 0, st>>>(a, (int)ch0);
+                e = hipGetLastError();
+            }
+        }
+    } else {
+        if (e == hipSuccess) e = launch_tier<D, 2>(a, nl, GM, st);
+        if (e == hipSuccess) e = launch_tier<D, 0>(a, nl, GM, st);
+    }
     if (e != hipSuccess) return e;
     merge_kernel<D><<<dim3((unsigned)a.Hq, (unsigned)nl), 64, 0, st>>>(a.part, a.NC, a.Hq, out,
                                                                       lse);
