@@ -2,6 +2,8 @@
 oracle's when both are fed the same fp32 scores (ties, zeros, sinks, 2-tier,
 ragged and maximum request sizes)."""
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -76,3 +78,95 @@ def test_assign_deterministic():
         outs.append((m, o))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def _check_assignment(scores, sinks, counts, gm, go, chunk=1 << 25, threads=16):
+    """Everything the assignment's definition fixes, checked without a sort:
+    the tier counts, the sinks at fp16, slots numbering each tier's tokens in
+    token order, order the inverse of (tier, slot), and the ranking across
+    every tier boundary - the last-ranked non-sink token of a tier (lowest
+    score, then highest index) ranks before the first of the next tier
+    (highest score, then lowest index).  Chunks of tokens are checked on
+    threads (numpy releases the interpreter lock); a first pass counts each
+    chunk's tiers so that every chunk knows where its slots start."""
+    n = scores.shape[0]
+    counts = np.asarray(counts, dtype=np.int64)
+    base = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+    spans = [(a, min(n, a + chunk)) for a in range(0, n, chunk)]
+
+    def tiers(a, b):
+        return (gm[a:b] >> 30).astype(np.int8)
+
+    def count(span):
+        return np.bincount(tiers(*span), minlength=4)[:4].astype(np.int64)
+
+    def check(arg):
+        (a, b), start = arg
+        t = tiers(a, b)
+        slot = (gm[a:b] & 0x3FFFFFFF).astype(np.int64)
+        js = np.arange(a, b, dtype=np.int64)
+        if a < sinks:
+            assert np.all(t[:sinks - a] == 0), "a sink is not fp16"
+        assert np.array_equal(go[base[t] + slot], js.astype(np.uint32)), "order is not the inverse of map"
+        s = scores[a:b]
+        ends = []
+        for q in range(4):
+            idx = np.nonzero(t == q)[0]
+            assert np.array_equal(slot[idx], start[q] + np.arange(idx.size)), \
+                f"tier {q}: slots out of token order"
+            idx = idx[js[idx] >= sinks]
+            if idx.size == 0:
+                ends.append(None)
+                continue
+            sq, jq = s[idx], js[idx]
+            lo, hi = sq.min(), sq.max()
+            ends.append(((float(lo), int(jq[sq == lo].max())), (float(hi), int(jq[sq == hi].min()))))
+        return ends
+
+    with ThreadPoolExecutor(threads) as ex:
+        per = np.array(list(ex.map(count, spans)))
+        assert np.array_equal(per.sum(axis=0), counts), \
+            f"tier counts {per.sum(axis=0).tolist()} != plan {counts.tolist()}"
+        starts = np.cumsum(per, axis=0) - per
+        results = list(ex.map(check, zip(spans, starts)))
+    worst, best = [None] * 4, [None] * 4   # (score, index) of each tier's two ends
+    for ends in results:
+        for q, e in enumerate(ends):
+            if e is None:
+                continue
+            w, bb = e
+            if worst[q] is None or (w[0], -w[1]) < (worst[q][0], -worst[q][1]):
+                worst[q] = w
+            if best[q] is None or (bb[0], -bb[1]) > (best[q][0], -best[q][1]):
+                best[q] = bb
+    present = [q for q in range(4) if worst[q] is not None]
+    for u, v in zip(present, present[1:]):
+        (ws, wj), (bs, bj) = worst[u], best[v]
+        assert ws > bs or (ws == bs and wj < bj), \
+            f"tier {u}'s last token ({ws}, {wj}) does not rank before tier {v}'s first ({bs}, {bj})"
+
+def test_assign_at_token_limit():
+    """The largest request a policy admits, n = 2^30 - 1 tokens (30 index bits
+    in the ranking key, slots up to 2^30 - 1), scores uniform fp32 draws with
+    only 2^24 distinct values (about 64 tokens share each value, so every
+    boundary falls inside a run of ties).  Three policies cover the int8 /
+    int4, fp16 / int8 and int8 / dropped boundaries.  The oracle's sort would
+    take minutes at this size, so the output is checked against everything
+    the definition fixes instead (_check_assignment)."""
+    n, S = (1 << 30) - 1, 4
+    rng = np.random.default_rng(30)
+    scores = rng.random(n, dtype=np.float32)
+    sd = to_dev(scores)
+    shape = sk.Shape(1, 1, 1, 64)
+    m = torch.empty(n, dtype=torch.int32, device="cuda")
+    o = torch.empty(n, dtype=torch.int32, device="cuda")
+    for b, three, overflow in ((0.45, 1, sk.OVERFLOW_REJECT), (0.7, 1, sk.OVERFLOW_REJECT),
+                               (0.3, 0, sk.OVERFLOW_DROP)):
+        pol = sk.Policy(n, S, three, b, overflow)
+        pl = sk.plan_make(shape, pol)
+        counts = np.array([pl.n16, pl.n8, pl.n4, pl.n_drop], dtype=np.int64)
+        say("assign at the token limit", dict(n=n, b=b, three=three, overflow=overflow,
+                                              counts=counts.tolist()))
+        sk.assign_tiers(pol, pl, sd, m, o)
+        torch.cuda.synchronize()
+        _check_assignment(scores, S, counts, u32(m), u32(o))
