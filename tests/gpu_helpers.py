@@ -82,6 +82,19 @@ def make_kv(seed, L, n, H, d):
     return K, V
 
 
+def make_kv_deep(seed, L, n, H, d):
+    """K, V for requests with very many layers: seeded normal rows in every
+    layer (fast), and the quantizer's edge rows in the first and last layers,
+    whose payload offsets are the extreme ones."""
+    rng = np.random.default_rng(seed)
+    K = (rng.standard_normal((L, n, H, d), dtype=np.float32) * 2.0).astype(np.float16)
+    V = (rng.standard_normal((L, n, H, d), dtype=np.float32) * 2.0).astype(np.float16)
+    for layer in (0, L - 1):
+        K[layer] = edge_rows(rng, n * H, d, 127).reshape(n, H, d)
+        V[layer] = edge_rows(rng, n * H, d, 7).reshape(n, H, d)
+    return K, V
+
+
 def tied_scores(seed, n):
     rng = np.random.default_rng(seed)
     s = rng.random(n).astype(np.float32) * 100

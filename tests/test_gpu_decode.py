@@ -18,7 +18,7 @@ from oracle import plan as OP
 from oracle import quant as OQ
 import serving_sk_score_amd as sk
 from workloads import gen, get_config
-from tests.gpu_helpers import Guarded, make_kv, say, tied_scores, to_dev
+from tests.gpu_helpers import Guarded, make_kv, make_kv_deep, say, tied_scores, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -67,11 +67,11 @@ CASES = [
 ]
 
 
-def _run(L, Hq, H, d, n, S, b, three, overflow, layers, seed=0):
+def _run(L, Hq, H, d, n, S, b, three, overflow, layers, seed=0, kv=make_kv):
     shape = sk.Shape(L, Hq, H, d)
     pl = sk.plan_make(shape, sk.Policy(n, S, three, b, overflow))
     opl = OP.make_plan(L, Hq, H, d, n, S, b, three, overflow)
-    K, V = make_kv(500 + n, L, n, H, d)
+    K, V = kv(500 + n, L, n, H, d)
     # keep the reconstruction finite: the edge rows reach the fp16 maximum
     K = np.clip(K.astype(np.float32), -1e3, 1e3).astype(np.float16)
     V = np.clip(V.astype(np.float32), -1e3, 1e3).astype(np.float16)
@@ -107,6 +107,16 @@ def test_decode_attention(case):
     if L > 1:
         o, lse, wo, wl, vmax = _run(*case, layers=(L - 1, 1))
         _check(o, lse, wo, wl, vmax, str(case) + " last layer")
+
+
+def test_decode_attention_at_layer_limit():
+    """All 65,535 layers a shape admits in one call (the layer is the third
+    dimension of the tier grids and the second of the merge's): fp16 sinks,
+    int8 and int4 tokens of an 11-token request."""
+    case = (65535, 4, 2, 64, 11, 2, 0.55, 1, 0)
+    say("decode at the layer limit", case)
+    o, lse, wo, wl, vmax = _run(*case, layers=(0, case[0]), kv=make_kv_deep)
+    _check(o, lse, wo, wl, vmax, str(case))
 
 
 def test_decode_nothing_sent():

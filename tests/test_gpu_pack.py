@@ -11,7 +11,7 @@ from oracle import plan as OP
 from oracle import quant as OQ
 import serving_sk_score_amd as sk
 from workloads import gen, get_config
-from tests.gpu_helpers import Guarded, fill_layers, make_kv, say, tied_scores, to_dev
+from tests.gpu_helpers import Guarded, fill_layers, make_kv, make_kv_deep, say, tied_scores, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -34,12 +34,12 @@ def _oracle_map(pl, n, seed):
     return amap, order
 
 
-def _run(L, Hq, H, d, n, S, b, three, seed=0):
+def _run(L, Hq, H, d, n, S, b, three, seed=0, kv=make_kv):
     say("pack/unpack", dict(L=L, Hq=Hq, H=H, d=d, n=n, S=S, b=b, three=three))
     shape = sk.Shape(L, Hq, H, d)
     pl = sk.plan_make(shape, sk.Policy(n, S, three, b))
     opl = OP.make_plan(L, Hq, H, d, n, S, b, three)
-    K, V = make_kv(seed + n, L, n, H, d)
+    K, V = kv(seed + n, L, n, H, d)
     amap, order = _oracle_map(opl, n, seed)
     want = OQ.pack(K, V, amap, opl)
     Kd, Vd = to_dev(K), to_dev(V)
@@ -88,6 +88,13 @@ def _run(L, Hq, H, d, n, S, b, three, seed=0):
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "L%d_Hq%d_H%d_d%d_n%d_S%d_b%s_t%d" % c)
 def test_pack_unpack_bitexact(case):
     _run(*case)
+
+
+def test_pack_unpack_at_layer_limit():
+    """65,535 layers, the most a shape admits (the layer is the second
+    dimension of every pack and unpack grid): fp16 sinks, int8 and int4 rows
+    of an 11-token request, bit-exact through pack, dense and paged unpack."""
+    _run(65535, 4, 2, 64, 11, 2, 0.55, 1, kv=make_kv_deep)
 
 
 def test_paged_skips_out_of_range_blocks():
