@@ -387,7 +387,9 @@ sk_status sk_upgrade_unpack(const sk_shape* shape, int64_t n_tokens, const void*
  * Arithmetic: q.k and p.v in fp32 from packed fp16 products; probabilities
  * are rounded to fp16 once (used in both the numerator and the
  * denominator), so o is a convex combination of the v_hat rows within
- * about 1e-3 * max|v_hat| of the exact value.  Deterministic. */
+ * about 1e-3 * max|v_hat| of the exact value.  Deterministic.
+ * Shapes with more than 65535 KV heads (a launch grid dimension) get 0 from
+ * the workspace query and SK_E_UNSUPPORTED from the call. */
 size_t    sk_decode_workspace_bytes(const sk_shape* shape, const sk_plan* plan,
                                     int32_t n_layers_q);
 sk_status sk_decode_attention(const sk_shape* shape, const sk_plan* plan, const void* payload,

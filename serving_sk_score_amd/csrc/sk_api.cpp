@@ -536,8 +536,13 @@ static size_t decode_ws(const sk_shape* shape, const sk_plan* plan, int32_t nl) 
                     (size_t)(shape->head_dim + 2) * sizeof(float));
 }
 
+// Decode launches put the KV head in a grid dimension, and its per-tile
+// buffer ranges assume at most that many heads.
+constexpr int32_t kMaxDecodeKvHeads = 65535;
+
 size_t sk_decode_workspace_bytes(const sk_shape* shape, const sk_plan* plan, int32_t nl) {
     if (check_shape(shape) || check_plan(plan, shape) || nl < 1 || nl > shape->n_layers) return 0;
+    if (shape->n_kv_heads > kMaxDecodeKvHeads) return 0;
     return decode_ws(shape, plan, nl);
 }
 
@@ -549,6 +554,8 @@ sk_status sk_decode_attention(const sk_shape* shape, const sk_plan* plan, const 
     if (nl < 1 || layer0 < 0 || (int64_t)layer0 + nl > shape->n_layers)
         return fail(SK_E_ARG, "layers [%d, %d + %d) outside [0, %d)", layer0, layer0, nl,
                     shape->n_layers);
+    if (shape->n_kv_heads > kMaxDecodeKvHeads)
+        return fail(SK_E_UNSUPPORTED, "decode: more than %d KV heads", kMaxDecodeKvHeads);
     if (!q || !out) return fail(SK_E_ARG, "q and out must be non-NULL");
     if (!aligned(q, 16)) return fail(SK_E_ARG, "q must be 16-byte aligned");
     if (!aligned(out, 4) || !aligned(lse, 4)) return fail(SK_E_ARG, "out and lse must be 4-byte aligned");

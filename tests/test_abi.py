@@ -201,6 +201,14 @@ def test_call_validation_without_device():
     assert lib.sk_decode_attention(B(shape), B(pc), FAKE, 0, 2, FAKE, FAKE, None, FAKE, dws - 1, None) == sk.SK_E_WORKSPACE
     assert lib.sk_decode_attention(B(shape), B(bad), FAKE, 0, 2, FAKE, FAKE, None, FAKE, dws, None) == sk.SK_E_ARG
     assert lib.sk_decode_attention(B(shape), B(pc), ctypes.c_void_p(0x7F0000001010), 0, 2, FAKE, FAKE, None, FAKE, dws, None) == sk.SK_E_ARG
+    # more KV heads than a decode launch grid holds
+    wide_kv = (1, 65536, 65536, 64)
+    wpc = _plan(wide_kv, (100, 4, 1, 0.5)).c
+    wshape, _ = _c(wide_kv)
+    assert lib.sk_decode_workspace_bytes(B(wshape), B(wpc), 1) == 0
+    assert lib.sk_decode_attention(B(wshape), B(wpc), FAKE, 0, 1, FAKE, FAKE, None, FAKE, 1 << 40, None) == sk.SK_E_UNSUPPORTED
+    ok_kv = (1, 65535, 65535, 64)
+    assert lib.sk_decode_workspace_bytes(B(_c(ok_kv)[0]), B(_plan(ok_kv, (100, 4, 1, 0.5)).c), 1) > 0
     assert lib.sk_pack(B(shape), B(bad), FAKE, FAKE, FAKE, None, FAKE, None) == sk.SK_E_ARG
     shape2, _ = _c((3, 4, 2, 64))
     assert lib.sk_pack(B(shape2), B(pc), FAKE, FAKE, FAKE, None, FAKE, None) == sk.SK_E_ARG
