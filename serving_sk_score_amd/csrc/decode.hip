@@ -79,36 +79,36 @@ __device__ __forceinline__ void deq8(uint32_t w, h2 s, uint32_t& lo, uint32_t& h
     hi = as_u32(b * s);
 }
 
-// (a & m) | c in one instruction.  Written out because the compiler splits
-// it into an and and an or when both constants are literals (a VOP3
-// instruction on this target takes no literal operand), and merges the mask
-// into a preceding xor instead.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
-    return r;
+// (w & m) ^ c in one v_bitop3_b32 (truth table 0x6A: bit (a << 2 | b << 1
+// | c) of the table is the result for operand bits a, b, c).
+__device__ __forceinline__ uint32_t and_xor(uint32_t w, uint32_t m, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(w, m, c, 0x6A);
 }
 
 // Eight int4 codes (element 2m in the low nibble of byte m) -> four dwords
 // of fp16 pairs, in the order (e0, e4), (e1, e5), (e2, e6), (e3, e7): the
 // pair of elements i and i + 4 sits at bits 4i and 4i + 16 of the dword, so
-// one v_and_or_b32 with a mask per pair places both nibbles under the 0x64
-// exponent bytes (bits 0-3 for even i after a shift by 8 for i >= 2).  The
-// low nibble of a byte gives 1024 + u, the high one 1024 + 16u, whose
-// packed fma with 1/16 (exact) and -72 returns u - 8 in one step.  The
-// caller keeps track of that channel order (q for K, the output for V).
+// one mask per pair places both nibbles under the 0x64 exponent bytes (bits
+// 0-3 for even i after a shift by 8 for i >= 2), and the same instruction
+// flips each nibble's top bit, turning the two's complement code into
+// u = code + 8: ((w ^ 0x88888888) & m) | 0x64006400 equals
+// (w & m) ^ ((0x88888888 & m) | 0x64006400) for every w, since the exponent
+// bits lie outside the mask (an xor there sets them as the or does, and
+// inside it the and and the xor commute).  The low nibble of a byte
+// gives 1024 + u, the high one 1024 + 16u, whose packed fma with 1/16
+// (exact) and -72 returns u - 8 in one step.  The caller keeps track of that
+// channel order (q for K, the output for V).
 __device__ __forceinline__ void deq4(uint32_t w, h2 s, uint32_t (&o)[4]) {
-    const uint32_t u = w ^ 0x88888888u;  // code + 8 per nibble
-    const uint32_t u2 = u >> 8;
+    const uint32_t w2 = w >> 8;
     const h2 lo_bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2 hi_mul = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h2 hi_bias = {(_Float16)-72.0f, (_Float16)-72.0f};
-    const h2 a0 = as_h2(and_or(u, 0x000F000Fu, 0x64006400u)) + lo_bias;    // e0, e4
-    const h2 a1 = __builtin_elementwise_fma(as_h2(and_or(u, 0x00F000F0u, 0x64006400u)), hi_mul,
-                                            hi_bias);                         // e1, e5
-    const h2 a2 = as_h2(and_or(u2, 0x000F000Fu, 0x64006400u)) + lo_bias;   // e2, e6
-    const h2 a3 = __builtin_elementwise_fma(as_h2(and_or(u2, 0x00F000F0u, 0x64006400u)), hi_mul,
-                                            hi_bias);                         // e3, e7
+    const h2 a0 = as_h2(and_xor(w, 0x000F000Fu, 0x64086408u)) + lo_bias;    // e0, e4
+    const h2 a1 = __builtin_elementwise_fma(as_h2(and_xor(w, 0x00F000F0u, 0x64806480u)), hi_mul,
+                                            hi_bias);                          // e1, e5
+    const h2 a2 = as_h2(and_xor(w2, 0x000F000Fu, 0x64086408u)) + lo_bias;   // e2, e6
+    const h2 a3 = __builtin_elementwise_fma(as_h2(and_xor(w2, 0x00F000F0u, 0x64806480u)), hi_mul,
+                                            hi_bias);                          // e3, e7
     o[0] = as_u32(a0 * s);
     o[1] = as_u32(a1 * s);
     o[2] = as_u32(a2 * s);
@@ -1076,14 +1076,14 @@ hipError_t launch_tier(const PartialArgs& a, int nl, int GM, hipStream_t st) {
             decode_mfma_kernel<D, TIER, true><<<grid, 64, 0, st>>>(a);
         else
             decode_mfma_kernel<D, TIER, false><<<grid, 64, 0, st>>>(a);
-        return hipGetLastError();
-    }
-    switch (GM) {
-        case 1: decode_partial_kernel<D, TIER, 1><<<grid, 64, 0, st>>>(a); break;
-        case 2: decode_partial_kernel<D, TIER, 2><<<grid, 64, 0, st>>>(a); break;
-        case 4: decode_partial_kernel<D, TIER, 4><<<grid, 64, 0, st>>>(a); break;
-        case 8: decode_partial_kernel<D, TIER, 8><<<grid, 64, 0, st>>>(a); break;
-        default: decode_partial_kernel<D, TIER, 16><<<grid, 64, 0, st>>>(a); break;
+    } else {
+        switch (GM) {
+            case 1: decode_partial_kernel<D, TIER, 1><<<grid, 64, 0, st>>>(a); break;
+            case 2: decode_partial_kernel<D, TIER, 2><<<grid, 64, 0, st>>>(a); break;
+            case 4: decode_partial_kernel<D, TIER, 4><<<grid, 64, 0, st>>>(a); break;
+            case 8: decode_partial_kernel<D, TIER, 8><<<grid, 64, 0, st>>>(a); break;
+            default: decode_partial_kernel<D, TIER, 16><<<grid, 64, 0, st>>>(a); break;
+        }
     }
     return hipGetLastError();
 }
