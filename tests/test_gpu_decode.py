@@ -64,6 +64,9 @@ CASES = [
     # enough chunks x layers (>= 512) for the one-wavefront-per-KV-head workgroups at d = 128
     (16, 32, 8, 128, 2048, 4, 0.5, 1, 0),    # G = 4, int8 tier: 32 chunks x 16 layers
     (16, 28, 4, 128, 2600, 4, 0.6, 0, 0),    # G = 7, 2-tier: int8 tier 33 chunks x 16 layers
+    # d = 256 with 32 KV heads: the widest token span the buffer-addressed
+    # tiles cover in these tests (2 x 32 rows a token), ragged last tile
+    (1, 32, 32, 256, 333, 4, 0.3, 1, 0),
 ]
 
 
