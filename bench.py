@@ -387,6 +387,11 @@ def run_batched(cfg, args, dev, torch, sk):
         "score_tflops": round(score_tflops, 1),
         "score_pct_mfma": round(score_tflops / MFMA_F16_PEAK_TFLOPS, 4),
         "score_flops_per_step": float(score_flops),
+        # the single-pass q.k count (half the two passes' flops), and the
+        # exponentials: one per causal (query, key) pair and pass
+        "score_tflops_single_pass": round(score_tflops / 2, 1),
+        "score_exps_per_step": float(score_flops / (2 * d)),
+        "score_gexp_per_s": round(score_flops / (2 * d) / score_s / 1e9, 1),
         "roofline": roof,
         "roofline_other_pass": dict(mfma_rl(*((rfl, rms) if dom == "colsum" else (cfl, cms)),
                                             names["rowlse" if dom == "colsum" else "colsum"],
@@ -497,6 +502,9 @@ def run_single(cfg, steps, warmup, dev, torch, sk, extras, per_layer=False):
                                      / 1e9 / HBM_PEAK_GBS, 4),
         "score_tflops": round(score_tflops, 1),
         "score_pct_mfma": round(score_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "score_tflops_single_pass": round(score_tflops / 2, 1),
+        "score_exps_per_step": float(L * pass_flops / d),
+        "score_gexp_per_s": round(L * pass_flops / d / (per["rowlse"] + per["colsum"]) / 1e9, 1),
         "roofline": dict(mfma_rl(*((cfl, cms) if dom == "colsum" else (rfl, rms)), names[dom],
                                  cfg.name), launches_per_step=L if per_layer else 1),
         "roofline_other_pass": dict(mfma_rl(*((rfl, rms) if dom == "colsum" else (cfl, cms)),
