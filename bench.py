@@ -134,6 +134,17 @@ def counted_traffic(kernel, workload):
     return None
 
 
+def step_spread(res, stages):
+    """Median and minimum over the timed steps of each stage's per-step time
+    (ms): res holds one {launch label: (ms array, work array)} per step and
+    a stage sums the launches of its labels within a step."""
+    out = {}
+    for name, labels in stages.items():
+        per_step = np.array([sum(float(r_[k][0].sum()) for k in labels) for r_ in res])
+        out[name] = [round(float(np.median(per_step)), 4), round(float(per_step.min()), 4)]
+    return out
+
+
 def hbm_rl(bytes_, sec, kernel, workload, launches=1):
     """Roofline entry of an HBM-bound kernel: algorithmic bytes per launch
     over its average launch time."""
@@ -403,6 +414,10 @@ def run_batched(cfg, args, dev, torch, sk):
                               "colsum": round(cms.sum() / K_, 3),
                               "pack": round(t_pack * 1e3, 3),
                               "unpack_paged": round(t_unp * 1e3, 3)},
+        "stage_ms_median_min": step_spread(res, {
+            "rowlse": ["rowlse"], "colsum": ["colsum"],
+            "pack": [f"pack@{b}" for b in cfg.budgets],
+            "unpack_paged": [f"unpack_paged@{b}" for b in cfg.budgets]}),
         "budgets": per_budget,
         "score_per_request": per_req,
         "cold_cache": "1 GiB write before each pack phase and each unpack phase",
@@ -517,6 +532,7 @@ def run_single(cfg, steps, warmup, dev, torch, sk, extras, per_layer=False):
             "unpack_paged": hbm_rl(paged_bytes, per["unpack_paged"],
                                    f"unpack_kernel<{d},{nbk},true>", cfg.name)},
         "stage_ms_per_step": {s: round(v * 1e3, 4) for s, v in per.items()},
+        "stage_ms_median_min": step_spread(res, {s: [s] for s in per}),
         "payload_bytes": plan.payload_bytes,
         "counts": {"fp16": plan.n16, "int8": plan.n8, "int4": plan.n4},
         "cold_cache": "1 GiB write before pack, unpack and paged unpack",

@@ -112,3 +112,14 @@ def test_roofline_arithmetic():
                       "batched_mix")
     assert m["achieved"] == 2000.0 and m["frac"] == 0.8
     assert m["flops_per_launch"] == 2e12 and m["avg_launch_ms"] == 1.0
+
+
+def test_step_spread_sums_a_stage_per_step():
+    """Per-stage median and minimum over steps, a stage summing its labels'
+    launches within each step."""
+    res = [{"a": (np.array([1.0, 2.0]), None), "b": (np.array([4.0]), None)},
+           {"a": (np.array([0.5]), None), "b": (np.array([1.0, 1.0]), None)},
+           {"a": (np.array([3.0]), None), "b": (np.array([0.0]), None)}]
+    out = bench.step_spread(res, {"a": ["a"], "ab": ["a", "b"]})
+    assert out["a"] == [3.0, 0.5]          # per step 3.0, 0.5, 3.0
+    assert out["ab"] == [3.0, 2.5]         # per step 7.0, 2.5, 3.0
