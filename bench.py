@@ -44,7 +44,9 @@ def parse():
     ap.add_argument("--others", default="gemma2_9b,qwen25_7b_2tier,mistral7b",
                     help="comma-separated single-request workloads measured after the "
                          "headline ('' for none)")
-    ap.add_argument("--other-steps", type=int, default=3)
+    ap.add_argument("--other-steps", type=int, default=3,
+                    help="timed steps of each single-request workload at least; more when "
+                         "that many take under 1 s (up to 20)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough budget of the oracle's timed sample")
@@ -429,7 +431,7 @@ def run_batched(cfg, args, dev, torch, sk):
 
 # ----------------------------------------------------------- single request --
 
-def run_single(cfg, steps, warmup, dev, torch, sk, extras, per_layer=False):
+def run_single(cfg, steps, warmup, dev, torch, sk, extras, per_layer=False, adapt=False):
     from workloads import gen_device as gd
 
     L, Hq, Hkv, d, n = cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.tokens
@@ -482,6 +484,17 @@ def run_single(cfg, steps, warmup, dev, torch, sk, extras, per_layer=False):
 
     for _ in range(warmup):
         step(untimed)
+    if adapt:
+        # a nested workload: one more untimed step, timed whole, sets the
+        # step count, at least `steps` and enough for 1 s of timed work, up
+        # to 20 steps (a headline run times exactly the steps asked for)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        step(untimed)
+        c1.record()
+        torch.cuda.synchronize()
+        steps = max(steps, min(20, int(np.ceil(1000.0 / max(c0.elapsed_time(c1), 1e-3)))))
     torch.cuda.synchronize()
     marks = [Marks(torch) for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
@@ -691,7 +704,8 @@ def main():
         for w in others:
             line["workloads"][w] = run_single(get_config(w), args.other_steps, 1, dev, torch, sk,
                                               extras=(w == "mistral7b"),
-                                              per_layer=args.score_launch == "per-layer")
+                                              per_layer=args.score_launch == "per-layer",
+                                              adapt=True)
             gc.collect()
             torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
