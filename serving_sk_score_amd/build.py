@@ -41,6 +41,16 @@ FLAGS = [
 ]
 
 
+# Flags for one source only.  The score passes take the iterative ILP
+# machine scheduler: it interleaves a unit's softmax with the next unit's
+# MFMAs better than the default one does (column pass 3-6% faster on the
+# Qwen- and Gemma-shaped layers and at 40K tokens, row pass within +-0.5%,
+# the same bits; no spills, two wavefronts per SIMD as before).
+SOURCE_FLAGS = {
+    "score.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -50,7 +60,7 @@ def hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

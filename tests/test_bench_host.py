@@ -86,16 +86,16 @@ def test_committed_traffic_tags_of_the_score_passes_are_current():
 
 def test_every_profiled_source_hash_is_current():
     """Every profile summary names the sha256 of the kernel source it was
-    taken on (traffic tags, and the counter summaries' source lines); each
-    must be the source as it is now, so a summary cannot outlive the code it
-    describes."""
+    taken on (traffic tags, and the counter summaries' source lines) and of
+    the build script whose flags compiled it; each must be the file as it is
+    now, so a summary cannot outlive the code it describes."""
     import re
     seen = 0
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         text = open(path).read()
         refs = re.findall(r"source=(\S+) sha256=([0-9a-f]{64})", text)
-        refs += re.findall(r"`?(serving_sk_score_amd/csrc/\w+\.(?:hip|cpp))`? sha256 `?([0-9a-f]{64})",
-                           text)
+        refs += re.findall(r"`?(serving_sk_score_amd/(?:csrc/\w+\.(?:hip|cpp)|build\.py))`? "
+                           r"sha256 `?([0-9a-f]{64})", text)
         for src, sha in refs:
             cur = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
             assert cur == sha, (os.path.basename(path), src)
